@@ -1,0 +1,252 @@
+"""CPU oracle for smoothed, quantised attention -- TEST INFRASTRUCTURE ONLY.
+
+Only tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg
+may import this package.  It wraps ``sage_oracle.c`` (plain C, fp64) through
+ctypes and shares no code with the HIP path.
+
+Every function follows one step of the method; see the header of
+``sage_oracle.c`` for the passages and readings.  Pins live in
+``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sage_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BQ, BK = 32, 64
+
+
+def build() -> str:
+    """Compile the oracle (gcc, OpenMP, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_dbl = ctypes.c_double
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    sig = {
+        "orc_bf16_value": ([ctypes.c_uint16], ctypes.c_float),
+        "orc_bf16_round": ([ctypes.c_float], ctypes.c_uint16),
+        "orc_e4m3_decode": ([ctypes.c_uint8], _dbl),
+        "orc_e4m3_encode": ([_dbl], ctypes.c_uint8),
+        "orc_i8_code": ([ctypes.c_float], _i32),
+        "orc_v_slot": ([_i32], _i32),
+        "orc_bf16_round_n": ([_vp, _vp, _i64], None),
+        "orc_e4m3_encode_n": ([_vp, _vp, _i64], None),
+        "orc_e4m3_decode_n": ([_vp, _vp, _i64], None),
+        "orc_k_mean": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp], _i32),
+        "orc_k_center": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp], None),
+        "orc_quant_i8_blocks": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp], None),
+        "orc_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                          _vp, _vp, _vp, _vp, _vp], _i32),
+        "orc_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
+        "orc_online_softmax_pv": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp], None),
+        "orc_attn_tiled": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _dbl, _i32,
+                            _vp, _i32, _vp], None),
+        "orc_attn_exact": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                            _i32, _i32, _i32, _i32, _dbl, _vp, _i32, _vp], None),
+        "orc_num_threads": ([], _i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bf16_view(t):
+    """A bf16 torch CPU tensor [B, N, H, D] (any strides, d-stride 1) -> (uint16 base
+    array keeping the storage alive, element strides (sb, sn, sh))."""
+    import torch
+    assert t.dtype == torch.bfloat16 and t.device.type == "cpu" and t.dim() == 4
+    assert t.stride(3) == 1
+    base = t.view(torch.int16).numpy()  # shares memory, keeps strides
+    return base, t.stride(0), t.stride(1), t.stride(2)
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
+
+
+# ---- codecs --------------------------------------------------------------
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_bf16_round_n(_p(x), _p(y), x.size)
+    return y
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty(x.shape, dtype=np.uint8)
+    _load().orc_e4m3_encode_n(_p(x), _p(y), x.size)
+    return y
+
+
+def e4m3_decode(c: np.ndarray) -> np.ndarray:
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    y = np.empty(c.shape, dtype=np.float64)
+    _load().orc_e4m3_decode_n(_p(c), _p(y), c.size)
+    return y
+
+
+def i8_code(x: float) -> int:
+    return _load().orc_i8_code(x)
+
+
+def v_slot(t: int) -> int:
+    return _load().orc_v_slot(t)
+
+
+# ---- quantisation ----------------------------------------------------------
+
+def quant_qk(q, k):
+    """Fused steps 1-4.  Returns dict of numpy arrays:
+    q_i8 / k_i8 [B,H,N,D] int8, q_scale [B,H,ceil(N/32)], k_scale [B,H,ceil(N/64)] fp32,
+    k_mean [B,H,D] uint16 (bf16 bits), inexact (int: channels with a non-exact sum)."""
+    B, N, H, D = q.shape
+    qb, qsb, qsn, qsh = _bf16_view(q)
+    kb, ksb, ksn, ksh = _bf16_view(k)
+    out = dict(
+        q_i8=np.empty((B, H, N, D), np.int8),
+        q_scale=np.empty((B, H, math.ceil(N / BQ)), np.float32),
+        k_i8=np.empty((B, H, N, D), np.int8),
+        k_scale=np.empty((B, H, math.ceil(N / BK)), np.float32),
+        k_mean=np.empty((B, H, D), np.uint16),
+    )
+    bad = _load().orc_quant_qk(_p(qb), qsb, qsn, qsh, _p(kb), ksb, ksn, ksh, B, N, H, D,
+                               _p(out["q_i8"]), _p(out["q_scale"]), _p(out["k_i8"]),
+                               _p(out["k_scale"]), _p(out["k_mean"]))
+    out["inexact"] = int(bad)
+    return out
+
+
+def k_mean(k):
+    B, N, H, D = k.shape
+    kb, sb, sn, sh = _bf16_view(k)
+    m = np.empty((B, H, D), np.uint16)
+    bad = _load().orc_k_mean(_p(kb), sb, sn, sh, B, N, H, D, _p(m))
+    return m, int(bad)
+
+
+def k_center(k, mean: np.ndarray) -> np.ndarray:
+    """bf16 bits of bf16(K - mean), contiguous [B,N,H,D]."""
+    B, N, H, D = k.shape
+    kb, sb, sn, sh = _bf16_view(k)
+    mean = np.ascontiguousarray(mean, dtype=np.uint16)
+    kc = np.empty((B, N, H, D), np.uint16)
+    _load().orc_k_center(_p(kb), sb, sn, sh, B, N, H, D, _p(mean), _p(kc))
+    return kc
+
+
+def quant_i8_blocks(x_bits: np.ndarray, blk: int):
+    """Per-block INT8 of a contiguous bf16-bits array [B,N,H,D]."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    B, N, H, D = x_bits.shape
+    codes = np.empty((B, H, N, D), np.int8)
+    scales = np.empty((B, H, math.ceil(N / blk)), np.float32)
+    _load().orc_quant_i8_blocks(_p(x_bits), N * H * D, H * D, D, B, N, H, D, blk,
+                                _p(codes), _p(scales))
+    return codes, scales
+
+
+def quant_v(v):
+    """Steps 5-6.  Returns dict: v_fp8 [B,H,D,Np] uint8 (slot-permuted, zero pad),
+    v_scale / v_mean [B,H,D] fp32, bad (int)."""
+    B, N, H, D = v.shape
+    vb, sb, sn, sh = _bf16_view(v)
+    Np = math.ceil(N / 64) * 64
+    out = dict(
+        v_fp8=np.empty((B, H, D, Np), np.uint8),
+        v_scale=np.empty((B, H, D), np.float32),
+        v_mean=np.empty((B, H, D), np.float32),
+    )
+    bad = _load().orc_quant_v(_p(vb), sb, sn, sh, B, N, H, D, _p(out["v_fp8"]),
+                              _p(out["v_scale"]), _p(out["v_mean"]))
+    out["bad"] = int(bad)
+    return out
+
+
+# ---- attention -------------------------------------------------------------
+
+def online_softmax_pv(s: np.ndarray, vals: np.ndarray, bc: int, quant_p: bool) -> np.ndarray:
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    vals = np.ascontiguousarray(vals, dtype=np.float64)
+    n, dv = vals.shape
+    assert s.shape == (n,)
+    out = np.empty(dv, np.float64)
+    _load().orc_online_softmax_pv(_p(s), _p(vals), n, dv, bc, int(bool(quant_p)), _p(out))
+    return out
+
+
+def _rows(N, rows):
+    if rows is None:
+        rows = np.arange(N, dtype=np.int32)
+    return np.ascontiguousarray(rows, dtype=np.int32)
+
+
+def attn_tiled(qk: dict, v: dict, sm_scale: float | None = None, rows=None, bc: int = BK):
+    """Step 7 (quantised path, fp64).  Returns fp64 [B,H,len(rows),D]."""
+    B, H, N, D = qk["q_i8"].shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    rows = _rows(N, rows)
+    out = np.empty((B, H, rows.size, D), np.float64)
+    arrs = [np.ascontiguousarray(qk["q_i8"]), np.ascontiguousarray(qk["q_scale"]),
+            np.ascontiguousarray(qk["k_i8"]), np.ascontiguousarray(qk["k_scale"]),
+            np.ascontiguousarray(v["v_fp8"]), np.ascontiguousarray(v["v_scale"]),
+            np.ascontiguousarray(v["v_mean"])]
+    _load().orc_attn_tiled(*[_p(a) for a in arrs], B, N, H, D, float(sm_scale), bc,
+                           _p(rows), rows.size, _p(out))
+    return out
+
+
+def attn_exact(q, k, v, sm_scale: float | None = None, rows=None):
+    """Step 8: exact fp64 softmax attention on the original bf16 inputs.
+    Returns fp64 [B,H,len(rows),D]."""
+    B, N, H, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    rows = _rows(N, rows)
+    qb, qsb, qsn, qsh = _bf16_view(q)
+    kb, ksb, ksn, ksh = _bf16_view(k)
+    vb, vsb, vsn, vsh = _bf16_view(v)
+    out = np.empty((B, H, rows.size, D), np.float64)
+    _load().orc_attn_exact(_p(qb), qsb, qsn, qsh, _p(kb), ksb, ksn, ksh, _p(vb), vsb, vsn, vsh,
+                           B, N, H, D, float(sm_scale), _p(rows), rows.size, _p(out))
+    return out
+
+
+def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm((x - ref).ravel()) / np.linalg.norm(ref.ravel()))

@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs shaped like the DiT attention workloads.
+
+The generator draws standard normals from a counter-based stream (synth.c) and
+maps them to per-tensor value distributions.  It holds none of the attention
+method's arithmetic; the fp32 -> bf16 step is torch's own round-to-nearest-even
+cast.  Both the HIP path and the CPU oracle consume these tensors.
+
+Workloads (shapes from the FLUX.3 Action RTX 5090 report, §02 stage 03, and the
+MiniMax H3 on DGX Spark page, "fixed workload"; distributions are the stated
+synthetic recipe, N(mean, variance)):
+
+  0 tiny         B1 H2  N256   D64   Q,K,V~N(0,1); K += off~N(0,4)
+  1 flux_joint   B2 H24 N4608  D128  Q,K~N(0,1), 31 (h,d) outlier channels x8;
+                                     K += off~N(0,3); V += off~N(0,1)
+  2 video_early  B2 H24 N3128  D128  as flux_joint
+  3 long_t2v     B1 H40 N32760 D128  Q,K~N(0,1); K += off~N(0,4); V += off~N(0,0.5)
+  4 quant_long   B1 H40 N32760 D128  Q,K,V~N(0,1) + off~N(0,4) on each
+
+Per-channel offsets and outlier multipliers are indexed by (h, d) and shared by
+every batch entry and token.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+
+STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
+STREAM_K_OFF, STREAM_V_OFF, STREAM_Q_OFF = 4, 5, 6
+STREAM_OUTLIER = 7
+
+
+def build() -> str:
+    """Compile synth.c into libsynth.so next to it (gcc, OpenMP)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        u64, i64, dbl = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double
+        vp = ctypes.c_void_p
+        lib.synth_u64.argtypes = [u64, u64, u64, i64, i64, vp]
+        lib.synth_normal_f64.argtypes = [u64, u64, u64, i64, i64, vp]
+        lib.synth_fill_f32.argtypes = [u64, u64, u64, i64, dbl, vp, vp, i64, vp]
+        for f in (lib.synth_u64, lib.synth_normal_f64, lib.synth_fill_f32):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def draws_u64(seed: int, config: int, stream: int, count: int, start: int = 0) -> np.ndarray:
+    out = np.empty(count, dtype=np.uint64)
+    _load().synth_u64(seed, config, stream, start, count, _ptr(out))
+    return out
+
+
+def normals(seed: int, config: int, stream: int, count: int, start: int = 0) -> np.ndarray:
+    out = np.empty(count, dtype=np.float64)
+    _load().synth_normal_f64(seed, config, stream, start, count, _ptr(out))
+    return out
+
+
+@dataclass(frozen=True)
+class Dist:
+    """sigma * z * (8 on outlier channels) + offset[h,d],  offset ~ N(0, off_var)."""
+    var: float = 1.0
+    outliers: bool = False
+    off_var: Optional[float] = None
+
+
+@dataclass(frozen=True)
+class Config:
+    idx: int
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    q: Dist = field(default_factory=Dist)
+    k: Dist = field(default_factory=Dist)
+    v: Dist = field(default_factory=Dist)
+    outlier_frac: float = 0.01
+    outlier_mult: float = 8.0
+
+    @property
+    def shape(self):
+        return (self.B, self.N, self.H, self.D)
+
+
+_FLUX_Q = Dist(1.0, outliers=True)
+_FLUX_K = Dist(1.0, outliers=True, off_var=3.0)
+_FLUX_V = Dist(1.0, off_var=1.0)
+
+CONFIGS = (
+    Config(0, "tiny", 1, 2, 256, 64, q=Dist(1.0), k=Dist(1.0, off_var=4.0), v=Dist(1.0)),
+    Config(1, "flux_joint", 2, 24, 4608, 128, q=_FLUX_Q, k=_FLUX_K, v=_FLUX_V),
+    Config(2, "video_early", 2, 24, 3128, 128, q=_FLUX_Q, k=_FLUX_K, v=_FLUX_V),
+    Config(3, "long_t2v", 1, 40, 32760, 128, q=Dist(1.0), k=Dist(1.0, off_var=4.0),
+           v=Dist(1.0, off_var=0.5)),
+    Config(4, "quant_long", 1, 40, 32760, 128, q=Dist(1.0, off_var=4.0),
+           k=Dist(1.0, off_var=4.0), v=Dist(1.0, off_var=4.0)),
+)
+
+
+def config(idx_or_name) -> Config:
+    for c in CONFIGS:
+        if c.idx == idx_or_name or c.name == idx_or_name:
+            return c
+    raise KeyError(idx_or_name)
+
+
+def custom(B: int, N: int, H: int, D: int, q: Dist = Dist(), k: Dist = Dist(1.0, off_var=4.0),
+           v: Dist = Dist(1.0, off_var=1.0), tag: int = 100) -> Config:
+    """An ad-hoc shape; `tag` keys the random streams (distinct from configs 0-4)."""
+    return Config(tag, f"custom{tag}", B, H, N, D, q=q, k=k, v=v)
+
+
+def outlier_channels(cfg: Config, seed: int = 0) -> np.ndarray:
+    """round(frac * H * D) distinct flat (h*D + d) indices: those with the smallest draws."""
+    n_chan = cfg.H * cfg.D
+    n_out = int(round(cfg.outlier_frac * n_chan))
+    r = draws_u64(seed, cfg.idx, STREAM_OUTLIER, n_chan)
+    return np.sort(np.argsort(r, kind="stable")[:n_out])
+
+
+def _channel_terms(cfg: Config, dist: Dist, off_stream: int, seed: int):
+    n_chan = cfg.H * cfg.D
+    scale = None
+    if dist.outliers:
+        scale = np.ones(n_chan, dtype=np.float64)
+        scale[outlier_channels(cfg, seed)] = cfg.outlier_mult
+    off = None
+    if dist.off_var is not None:
+        off = normals(seed, cfg.idx, off_stream, n_chan) * math.sqrt(dist.off_var)
+    return scale, off
+
+
+def fill_f32(cfg: Config, which: str, seed: int = 0) -> np.ndarray:
+    """fp32 values of one tensor ('q', 'k' or 'v'), row-major [B, N, H, D]."""
+    dist = {"q": cfg.q, "k": cfg.k, "v": cfg.v}[which]
+    stream = {"q": STREAM_Q, "k": STREAM_K, "v": STREAM_V}[which]
+    off_stream = {"q": STREAM_Q_OFF, "k": STREAM_K_OFF, "v": STREAM_V_OFF}[which]
+    scale, off = _channel_terms(cfg, dist, off_stream, seed)
+    count = cfg.B * cfg.N * cfg.H * cfg.D
+    out = np.empty(count, dtype=np.float32)
+    _load().synth_fill_f32(seed, cfg.idx, stream, count, math.sqrt(dist.var), _ptr(scale),
+                           _ptr(off), cfg.H * cfg.D, _ptr(out))
+    return out.reshape(cfg.shape)
+
+
+def make_qkv(cfg, seed: int = 0, device=None):
+    """(q, k, v) as bf16 torch tensors [B, N, H, D] (contiguous NHD)."""
+    import torch
+    if not isinstance(cfg, Config):
+        cfg = config(cfg)
+    out = []
+    for which in ("q", "k", "v"):
+        t = torch.from_numpy(fill_f32(cfg, which, seed))
+        if device is not None:
+            t = t.to(device)
+        out.append(t.to(torch.bfloat16))
+    return tuple(out)
+
+
+def query_subset(N: int, every: int = 8, block: int = 32) -> np.ndarray:
+    """Stratified query rows: every `every`-th block of `block` queries, plus the last
+    (possibly partial) block.  Used where the oracle cannot afford all rows."""
+    nblk = (N + block - 1) // block
+    blocks = sorted(set(range(0, nblk, every)) | {nblk - 1})
+    rows = [r for b in blocks for r in range(b * block, min(N, (b + 1) * block))]
+    return np.asarray(rows, dtype=np.int32)

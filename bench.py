@@ -1,0 +1,241 @@
+"""Benchmark of the smoothed, quantised attention path on one MI355X.
+
+One step = sage_quant_qk + sage_quant_v + sage_attn_fwd over one batch of
+seeded synthetic bf16 inputs already resident in HBM (default workload: the
+FLUX.3 Action joint block, B2 H24 N4608 D128).  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload flux_joint]
+
+`value` is attention TFLOPS over the whole step, 4*B*H*N^2*D / step time (the
+quantisation kernels are inside the step).  Per-kernel times come from HIP
+events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-attention TFLOPS at N=4608 & 32760 (1 GPU); quant-kernel HBM GB/s"
+PEAK_MFMA_TFLOPS = 5000.0   # MI355X dense INT8 / FP8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def algorithmic(B, N, H, D):
+    """Algorithmic work of each kernel (what the method must do; no padding,
+    no second read of a two-pass design)."""
+    E = B * N * H * D
+    nq, nk = math.ceil(N / 32), math.ceil(N / 64)
+    return {
+        "attn_ops": 4.0 * B * H * N * N * D,
+        # Q: 2 B read + 1 B write per element + 4 B per 32-token block scale
+        "quant_q_bytes": 3.0 * E + 4.0 * B * H * nq,
+        # K: 2 B read + 1 B write per element + block scales + bf16 mean
+        "quant_k_bytes": 3.0 * E + 4.0 * B * H * nk + 2.0 * B * H * D,
+        # V: 2 B read + 1 B write per element + fp32 mean and scale per channel
+        "quant_v_bytes": 3.0 * E + 8.0 * B * H * D,
+    }
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_record(kernel_src):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "attn_fwd_flux_joint_counters.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(workload_cfg, seed=0):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    full Q/K and V quantisation plus the tiled attention for every 18th
+    32-query block of every head; scaled to a whole-step estimate."""
+    import numpy as np
+    import oracle
+    import synth
+    cfg = workload_cfg
+    q, k, v = synth.make_qkv(cfg, seed)
+    t0 = time.perf_counter()
+    qk = oracle.quant_qk(q, k)
+    vq = oracle.quant_v(v)
+    t_quant = time.perf_counter() - t0
+    nb = math.ceil(cfg.N / 32)
+    blocks = list(range(0, nb, 18))
+    rows = np.array([r for b in blocks for r in range(32 * b, min(cfg.N, 32 * b + 32))], np.int32)
+    t0 = time.perf_counter()
+    oracle.attn_tiled(qk, vq, rows=rows)
+    t_attn = time.perf_counter() - t0
+    est = t_quant + t_attn * cfg.N / rows.size
+    ops = algorithmic(cfg.B, cfg.N, cfg.H, cfg.D)["attn_ops"]
+    return {
+        "value": round(ops / est / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"full Q/K/V quantisation ({t_quant:.2f} s) + tiled attention on "
+                   f"{rows.size}/{cfg.N} query rows of all {cfg.B * cfg.H} heads "
+                   f"({t_attn:.2f} s), scaled to the whole step ({est:.1f} s est.)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux_joint",
+                    choices=["tiny", "flux_joint", "video_early", "long_t2v", "quant_long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the path shards over (batch, head) with no "
+              "exchange, and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import quantized_attention_video_smooth_amd as sage
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = sage.lib()
+    cfg = synth.config(args.workload)
+    B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
+    Np = sage.sage_padded_tokens(N)
+    dev = torch.device("cuda:0")
+    q, k, v = synth.make_qkv(cfg, args.seed, device=dev)
+    q_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+    q_scale = torch.empty((B, H, Np // 32), dtype=torch.float32, device=dev)
+    k_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+    k_scale = torch.empty((B, H, Np // 64), dtype=torch.float32, device=dev)
+    k_mean = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    v_fp8 = torch.empty((B, H, D, Np), dtype=torch.uint8, device=dev)
+    v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    v_mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
+    ws_qk = torch.empty(sage.sage_quant_qk_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(sage.sage_quant_v_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    qs, ks, vs, os_ = q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3]
+    do_attn = args.workload != "quant_long"
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        st = lib.sage_quant_qk(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, q_i8.data_ptr(),
+                               q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
+                               k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), sp)
+        if evs:
+            evs[1].record(stream)
+        st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
+                               v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), sp)
+        if evs:
+            evs[2].record(stream)
+        if do_attn:
+            st |= lib.sage_attn_fwd(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
+                                    k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
+                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, sp)
+        if evs:
+            evs[3].record(stream)
+        if st != 0:
+            raise RuntimeError(f"libsage call failed with status {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, synchronised on both sides.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # Per-kernel durations (separate pass, events between the calls).
+    per = {"quant_qk": [], "quant_v": [], "attn_fwd": []}
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(evs)
+        torch.cuda.synchronize()
+        per["quant_qk"].append(evs[0].elapsed_time(evs[1]))
+        per["quant_v"].append(evs[1].elapsed_time(evs[2]))
+        per["attn_fwd"].append(evs[2].elapsed_time(evs[3]))
+    med = {k2: sorted(v2)[len(v2) // 2] for k2, v2 in per.items()}
+    avg = {k2: sum(v2) / len(v2) for k2, v2 in per.items()}
+
+    work = algorithmic(B, N, H, D)
+    step_s = ms_per_step * 1e-3
+    if do_attn:
+        value = work["attn_ops"] / step_s / 1e12
+        attn_tflops = work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12
+        roofline = {
+            "kernel": "sage_attn_fwd (attn_fwd_kernel<128>)",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
+            "traffic": traffic_record(os.path.join(ROOT, "quantized_attention_video_smooth_amd",
+                                                   "csrc", "sage_attn.hip")),
+        }
+        unit = "TFLOPS"
+    else:
+        qv_bytes = work["quant_q_bytes"] + work["quant_k_bytes"] + work["quant_v_bytes"]
+        value = qv_bytes / step_s / 1e9
+        gbs = (work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9
+        roofline = {"kernel": "sage_quant_qk", "bound": "hbm", "achieved": round(gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": None}
+        unit = "GB/s"
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 QK / fp8-e4m3 PV, fp32 softmax+accum",
+        "data": "synthetic (seeded counter-based normals, bf16 NHD)",
+        "config": {"workload": cfg.name, "B": B, "N": N, "H": H, "D": D, "causal": False,
+                   "layout": "NHD bf16 in, bf16 out", "seed": args.seed},
+        "kernels_ms": {k2: {"avg": round(avg[k2], 5), "median": round(med[k2], 5)} for k2 in per},
+        "attn_tflops": round(work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12, 2) if do_attn else None,
+        "quant_qk_gbs": round((work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9, 1),
+        "quant_v_gbs": round(work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

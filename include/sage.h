@@ -1,0 +1,197 @@
+/*
+ * sage.h -- C ABI of libsage.so: smoothed, quantised attention for MI355X
+ * (gfx950), in the manner of SageAttention2 as used in the FLUX.3 Action and
+ * MiniMax-H3 DiT blocks.
+ *
+ * Source pages (cited by title and section):
+ *   "FLUX.3 Action RTX 5090 report", §02 Engineering: stage 03 "SageAttention2"
+ *     (per-block INT8 QK, FP8 PV, FP32 accumulation, K smooth and V smooth kept,
+ *     NHD layout); stage 04 (fusions bit-exact against the unfused path);
+ *     card A (K centring fused into the INT8 quantiser, BF16 rounding kept);
+ *     card B (producers write BF16 NHD directly); card C (V read as a slice of
+ *     the V+MLP projection; tiled transpose, padding and permutation).
+ *   "MiniMax H3 on DGX Spark", §01 precision map (QK INT8 / PV FP8).
+ *   "Why can an A10 run FLUX.1", §1.1 (E4M3: 4 exponent, 3 mantissa bits).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors named "[B,N,H,D]" are bf16 (uint16 bit patterns) in token-major
+ *     NHD order with element strides (sb, sn, sh) and unit stride over d.
+ *     Strides may describe a view into a wider buffer (e.g. V as a column slice
+ *     of a fused projection output).
+ *   - Np = N rounded up to a multiple of 64 (sage_padded_tokens).
+ *   - Pointers marked "device" are HIP device pointers; `stream` is a
+ *     hipStream_t passed as void* (NULL = the null stream).
+ *   - The caller owns every buffer; the library allocates no device memory
+ *     and keeps no per-call state.  Calls are asynchronous: they enqueue work on
+ *     `stream` and return; buffers must stay valid until the stream reaches it.
+ *   - Validation runs first; on failure a negative status is returned and
+ *     nothing is enqueued.  Nothing throws or aborts across the ABI.  A launch
+ *     failure returns SAGE_ERR_HIP.  NaN / Inf inputs give unspecified values.
+ *   - Supported: D in {64, 128}; B, N, H >= 1; B*H*Np*D < 2^31; all base
+ *     pointers and input strides 16-byte aligned (strides multiple of 8).
+ *   - Inputs and outputs must not overlap (checked by address range).
+ *   - The library is reentrant.  Quantised outputs are bit-deterministic;
+ *     the attention output is bit-deterministic for a given build.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sage_status {
+  SAGE_OK = 0,
+  SAGE_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  SAGE_ERR_SHAPE = -2,       /* B, N or H < 1, or the problem is too large       */
+  SAGE_ERR_UNSUPPORTED = -3, /* D not in {64, 128}                               */
+  SAGE_ERR_STRIDE = -4,      /* a stride is not positive                         */
+  SAGE_ERR_ALIGN = -5,       /* a pointer or stride breaks 16-byte alignment     */
+  SAGE_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required       */
+  SAGE_ERR_OVERLAP = -7,     /* an output overlaps an input or another output    */
+  SAGE_ERR_HIP = -8          /* a HIP launch or runtime call failed              */
+};
+
+#define SAGE_BQ 32          /* Q quantisation block, tokens (one MFMA column tile) */
+#define SAGE_BK 64          /* K quantisation block = attention key tile, tokens   */
+#define SAGE_NPAD 64        /* token padding of the quantised layouts              */
+#define SAGE_PERM_VERSION 1 /* version of the V slot map below                     */
+
+typedef struct {
+  int32_t bq;             /* SAGE_BQ */
+  int32_t bk;             /* SAGE_BK */
+  int32_t n_pad_multiple; /* SAGE_NPAD */
+  int32_t perm_version;   /* SAGE_PERM_VERSION */
+} sage_layout;
+
+/* Fills *out (host pointer) with the layout constants.  Returns SAGE_OK or
+ * SAGE_ERR_NULL. */
+int sage_get_layout(sage_layout* out);
+
+/* N rounded up to a multiple of 64 (N >= 0). */
+int64_t sage_padded_tokens(int64_t N);
+
+/* Storage slot of token t (0..63) inside a 64-token block of the transposed V
+ * (card C's "permutation"; the page does not define it).  Version 1:
+ *     slot bits (5..0) = token bits (2, 5, 4, 3, 1, 0)
+ * i.e. slot = 32*t2 + 16*t5 + 8*t4 + 4*t3 + 2*t1 + t0.  With this order the
+ * 32 probabilities that one lane of the attention kernel holds after the INT8
+ * QK^T MFMA are exactly the 32 V bytes that lane feeds to the FP8 PV MFMA.
+ * Returns -1 for t outside 0..63. */
+int sage_v_slot(int t);
+
+/* Workspace (device memory, bytes) needed by sage_quant_qk / sage_quant_v:
+ * per-chunk channel partials (and, for V, the per-channel 448/a).  Any
+ * contents on entry; clobbered by the call.  One workspace must not be shared
+ * by calls that may run concurrently.  Returns 0 for unsupported shapes. */
+size_t sage_quant_qk_workspace_size(int B, int N, int H, int D);
+size_t sage_quant_v_workspace_size(int B, int N, int H, int D);
+
+/*
+ * sage_quant_qk -- K smoothing + INT8 K, and INT8 Q (report §02 stage 03;
+ * card A "K centering x INT8 quant").
+ *
+ *   k_mean[b,h,d] = bf16( fp32( (sum over all N tokens of K[b,n,h,d], fp64) / N ) )
+ *   kc            = bf16( fp32(K) - fp32(k_mean) )          (BF16 rounding kept)
+ *   per (b, h, 64-token block t):  a = max |kc|,  k_scale = a / 127,
+ *       k_i8 = clamp(rne(kc * (127 / a)), -127, 127)        (fp32 ops, RNE)
+ *   per (b, h, 32-token block s) of raw Q (no smoothing, no softmax scale):
+ *       q_scale = max|Q| / 127,  q_i8 = clamp(rne(Q * (127 / max|Q|)), -127, 127)
+ *   A block whose absmax is 0 (or whose 127/a overflows) gets scale 0, codes 0.
+ *   The last block of a sequence takes its absmax over valid tokens only.
+ *
+ * Inputs (device): q, k bf16 [B,N,H,D] with element strides (sb, sn, sh).
+ * Outputs (device, contiguous, written in full including padding):
+ *   q_i8    int8  [B,H,Np,D]   head-major; rows N..Np-1 are 0
+ *   q_scale fp32  [B,H,Np/32]  blocks past the end of the sequence are 0
+ *   k_i8    int8  [B,H,Np,D]   rows N..Np-1 are 0
+ *   k_scale fp32  [B,H,Np/64]
+ *   k_mean  bf16  [B,H,D]
+ * workspace: device, >= sage_quant_qk_workspace_size(B,N,H,D) bytes.
+ * The per-channel sums are exact whenever every value of a channel is a
+ * multiple of the channel's smallest non-zero bf16 ulp u and sum|x| < u * 2^52
+ * (true for all practical activations); the mean bits then do not depend on
+ * summation order.
+ */
+int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                  const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                  int B, int N, int H, int D,
+                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sage_quant_v -- V smoothing + FP8 E4M3 V, transposed, padded and permuted
+ * (report card C "V alias + tiled transpose"; E4M3 per the A10 FLUX.1 page §1.1).
+ *
+ *   v_mean[b,h,d]  = fp32( (sum over N tokens of V, fp64) / N )
+ *   a              = max(|max_n V - v_mean|, |min_n V - v_mean|)   (fp32)
+ *   v_scale[b,h,d] = a / 448
+ *   code           = E4M3FN( fp32(V - v_mean) * (448 / a) )  RNE, saturating,
+ *                    sign kept; a == 0 (or 448/a overflowing) gives scale 0 and
+ *                    codes 0x00.
+ *
+ * Input (device): v bf16 [B,N,H,D] with element strides; may alias a column
+ * slice of a wider projection output.
+ * Outputs (device, contiguous):
+ *   v_fp8   uint8 [B,H,D,Np]  token t of 64-block g at column 64*g + sage_v_slot(t % 64);
+ *                             padding columns hold 0x00
+ *   v_scale fp32  [B,H,D]
+ *   v_mean  fp32  [B,H,D]
+ * workspace: as for sage_quant_qk, sized by sage_quant_v_workspace_size.
+ */
+int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh,
+                 int B, int N, int H, int D,
+                 uint8_t* v_fp8, float* v_scale, float* v_mean,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sage_attn_fwd -- fused non-causal attention on the quantised operands
+ * (report §02 stage 03: INT8 QK, FP8 PV, FP32 accumulation, V smooth).
+ *
+ * For query i of head (b, h), over 64-key tiles in ascending order:
+ *   s_j = (sum_d q_i8[i,d] k_i8[j,d]) * q_scale[i/32] * k_scale[j/64] * sm_scale
+ *   m   = running row max including the current tile; alpha = exp(m_old - m)
+ *   p_j = exp(s_j - m);  l = alpha*l + sum p_j  (fp32, unquantised p)
+ *   acc = alpha*acc + sum_j E4M3(448 p_j) * E4M3 V_j   (FP8 MFMA, fp32 accum)
+ *   out[b,i,h,d] = bf16( acc[d] / (448 l) * v_scale[d] + v_mean[d] )   (RNE)
+ * Keys at or beyond N are masked out (excluded from max and sums).
+ *
+ * Inputs (device): the outputs of sage_quant_qk and sage_quant_v for the same
+ * B, N, H, D.  sm_scale <= 0 selects 1/sqrt(D).
+ * Output (device): out bf16 [B,N,H,D] with element strides (o_sb, o_sn, o_sh),
+ * unit stride over d (e.g. a contiguous NHD tensor).
+ */
+int sage_attn_fwd(const int8_t* q_i8, const float* q_scale,
+                  const int8_t* k_i8, const float* k_scale,
+                  const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
+                  int B, int N, int H, int D, float sm_scale,
+                  void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, void* stream);
+
+/* Host-only argument checks of the three entry points: same arguments (less
+ * the stream), same status codes, no HIP calls; usable without a GPU. */
+int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                           const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                           int B, int N, int H, int D,
+                           const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                           const float* k_scale, const uint16_t* k_mean,
+                           const void* workspace, size_t workspace_bytes);
+int sage_validate_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh,
+                          int B, int N, int H, int D,
+                          const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
+                          const void* workspace, size_t workspace_bytes);
+int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale,
+                           const int8_t* k_i8, const float* k_scale,
+                           const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
+                           int B, int N, int H, int D,
+                           const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh);
+
+/* Static, never-NULL description of a status code. */
+const char* sage_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_H */

@@ -1,0 +1,223 @@
+"""Python binding of libsage.so (smoothed, quantised attention on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/sage.h.  torch provides device memory and
+the current stream.  There is no fallback: if libsage.so is missing, importing
+the raw functions raises.
+
+Raw entry points keep the C names (sage_quant_qk, sage_quant_v,
+sage_attn_fwd, ...) and take integers (pointers, strides, sizes).  The
+tensor-level helpers quant_qk / quant_v / attn_fwd allocate outputs with
+torch.empty on the input's device and call the raw entry points on
+torch.cuda.current_stream().
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage.so")
+
+SAGE_OK = 0
+BQ, BK, NPAD = 32, 64, 64
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+_lock = threading.Lock()
+_vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+
+_SIGS = {
+    "sage_get_layout": ([_vp], _i32),
+    "sage_padded_tokens": ([_i64], _i64),
+    "sage_v_slot": ([_i32], _i32),
+    "sage_quant_qk_workspace_size": ([_i32] * 4, _sz),
+    "sage_quant_v_workspace_size": ([_i32] * 4, _sz),
+    "sage_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                       _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "sage_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "sage_attn_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                       _vp, _i64, _i64, _i64, _vp], _i32),
+    "sage_validate_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _sz], _i32),
+    "sage_validate_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz], _i32),
+    "sage_validate_attn_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                _vp, _i64, _i64, _i64], _i32),
+    "sage_status_string": ([_i32], ctypes.c_char_p),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsage.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(
+                        f"{LIB_PATH} is missing; build it with "
+                        "`python -m quantized_attention_video_smooth_amd.build`")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (args, res) in _SIGS.items():
+                    f = getattr(handle, name)
+                    f.argtypes = args
+                    f.restype = res
+                _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sage_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SAGE_OK:
+        raise SageError(status, where)
+
+
+# ---- raw C entry points (same names, integer arguments) ---------------------
+
+def sage_quant_qk(*args) -> int:
+    return lib().sage_quant_qk(*args)
+
+
+def sage_quant_v(*args) -> int:
+    return lib().sage_quant_v(*args)
+
+
+def sage_attn_fwd(*args) -> int:
+    return lib().sage_attn_fwd(*args)
+
+
+def sage_padded_tokens(n: int) -> int:
+    return lib().sage_padded_tokens(n)
+
+
+def sage_v_slot(t: int) -> int:
+    return lib().sage_v_slot(t)
+
+
+def sage_quant_qk_workspace_size(B: int, N: int, H: int, D: int) -> int:
+    return lib().sage_quant_qk_workspace_size(B, N, H, D)
+
+
+def sage_quant_v_workspace_size(B: int, N: int, H: int, D: int) -> int:
+    return lib().sage_quant_v_workspace_size(B, N, H, D)
+
+
+# ---- tensor-level helpers ---------------------------------------------------
+
+_workspaces: dict = {}
+
+
+def workspace(device, nbytes: int):
+    """A device scratch buffer of at least nbytes, cached per device; calls
+    sharing it must be ordered (one stream)."""
+    import torch
+    key = str(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _nhd(t, name):
+    import torch
+    if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1 or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA bf16 [B,N,H,D] tensor with unit stride over D")
+    return t.stride(0), t.stride(1), t.stride(2)
+
+
+def quant_qk(q, k, stream=None):
+    """K smoothing + INT8 K and INT8 Q.  Returns (q_i8 [B,H,Np,D], q_scale [B,H,Np/32],
+    k_i8 [B,H,Np,D], k_scale [B,H,Np/64], k_mean [B,H,D] bf16)."""
+    import torch
+    B, N, H, D = q.shape
+    if tuple(k.shape) != (B, N, H, D):
+        raise ValueError("q and k must have the same shape")
+    qs, ks = _nhd(q, "q"), _nhd(k, "k")
+    Np = sage_padded_tokens(N)
+    dev = q.device
+    q_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+    q_scale = torch.empty((B, H, Np // BQ), dtype=torch.float32, device=dev)
+    k_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+    k_scale = torch.empty((B, H, Np // BK), dtype=torch.float32, device=dev)
+    k_mean = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    need = sage_quant_qk_workspace_size(B, N, H, D)
+    ws = workspace(dev, need)
+    _check(sage_quant_qk(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D,
+                         q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
+                         k_mean.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)),
+           "sage_quant_qk")
+    return q_i8, q_scale, k_i8, k_scale, k_mean
+
+
+def quant_v(v, stream=None):
+    """V smoothing + FP8 E4M3 V, transposed and slot-permuted.  Returns
+    (v_fp8 [B,H,D,Np] uint8, v_scale [B,H,D], v_mean [B,H,D])."""
+    import torch
+    B, N, H, D = v.shape
+    vs = _nhd(v, "v")
+    Np = sage_padded_tokens(N)
+    dev = v.device
+    v_fp8 = torch.empty((B, H, D, Np), dtype=torch.uint8, device=dev)
+    v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    v_mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    need = sage_quant_v_workspace_size(B, N, H, D)
+    ws = workspace_v(dev, need)
+    _check(sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
+                        v_mean.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)),
+           "sage_quant_v")
+    return v_fp8, v_scale, v_mean
+
+
+_workspaces_v: dict = {}
+
+
+def workspace_v(device, nbytes: int):
+    """Separate cached workspace for sage_quant_v."""
+    import torch
+    key = str(device)
+    ws = _workspaces_v.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces_v[key] = ws
+    return ws
+
+
+def attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, N: int, sm_scale: float | None = None,
+             out=None, stream=None):
+    """Fused attention on the quantised operands; returns bf16 [B,N,H,D] (or fills `out`)."""
+    import torch
+    B, H, Np, D = q_i8.shape
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q_i8.device)
+    os_ = _nhd(out, "out")
+    _check(sage_attn_fwd(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
+                         v_fp8.data_ptr(), v_scale.data_ptr(), v_mean.data_ptr(), B, N, H, D,
+                         float(sm_scale) if sm_scale else 0.0, out.data_ptr(), *os_,
+                         _stream_ptr(stream)),
+           "sage_attn_fwd")
+    return out
+
+
+def sage_attention(q, k, v, sm_scale: float | None = None, stream=None):
+    """The whole path: quant_qk, quant_v, attn_fwd.  q, k, v bf16 [B,N,H,D]."""
+    qk = quant_qk(q, k, stream)
+    vq = quant_v(v, stream)
+    return attn_fwd(qk[0], qk[1], qk[2], qk[3], *vq, N=q.shape[1], sm_scale=sm_scale, stream=stream)

@@ -1,0 +1,218 @@
+// C ABI of libsage: argument validation and dispatch to the HIP launchers.
+// The contract of every function is documented in include/sage.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/sage.h"
+#include "sage_internal.h"
+
+namespace {
+
+using sage::ceil_div;
+using sage::padded_tokens;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  uintptr_t a = (uintptr_t)p;
+  return Range{a, a + bytes};
+}
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int B, int N, int H, int D) {
+  if (B < 1 || N < 1 || H < 1) return SAGE_ERR_SHAPE;
+  if (D != 64 && D != 128) return SAGE_ERR_UNSUPPORTED;
+  const int64_t elems = (int64_t)B * H * padded_tokens(N) * D;
+  if (elems >= ((int64_t)1 << 31)) return SAGE_ERR_SHAPE;
+  return SAGE_OK;
+}
+
+// Strides of size-1 dimensions are never used; the others must be positive
+// and keep 16-byte alignment of every 8-element (16-byte) row chunk.
+int check_strides(int B, int N, int H, int64_t sb, int64_t sn, int64_t sh) {
+  const int64_t s[3] = {B > 1 ? sb : 0, N > 1 ? sn : 0, H > 1 ? sh : 0};
+  const int sz[3] = {B, N, H};
+  for (int i = 0; i < 3; ++i) {
+    if (sz[i] > 1 && s[i] <= 0) return SAGE_ERR_STRIDE;
+    if (s[i] % 8 != 0) return SAGE_ERR_ALIGN;
+  }
+  return SAGE_OK;
+}
+
+// Bytes spanned by a bf16 [B,N,H,D] view.
+size_t view_bytes(int B, int N, int H, int D, int64_t sb, int64_t sn, int64_t sh) {
+  const int64_t last = (B > 1 ? (int64_t)(B - 1) * sb : 0) + (N > 1 ? (int64_t)(N - 1) * sn : 0) +
+                       (H > 1 ? (int64_t)(H - 1) * sh : 0) + D;
+  return (size_t)last * 2;
+}
+
+bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(outs[i], outs[j])) return true;
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int sage_get_layout(sage_layout* out) {
+  if (!out) return SAGE_ERR_NULL;
+  out->bq = SAGE_BQ;
+  out->bk = SAGE_BK;
+  out->n_pad_multiple = SAGE_NPAD;
+  out->perm_version = SAGE_PERM_VERSION;
+  return SAGE_OK;
+}
+
+int64_t sage_padded_tokens(int64_t N) { return N <= 0 ? 0 : padded_tokens(N); }
+
+int sage_v_slot(int t) {
+  if (t < 0 || t > 63) return -1;
+  return (((t >> 2) & 1) << 5) | (((t >> 5) & 1) << 4) | (((t >> 3) & 3) << 2) | (t & 3);
+}
+
+size_t sage_quant_qk_workspace_size(int B, int N, int H, int D) {
+  if (check_shape(B, N, H, D) != SAGE_OK) return 0;
+  return sage::qk_workspace(B, N, H, D).bytes;
+}
+
+size_t sage_quant_v_workspace_size(int B, int N, int H, int D) {
+  if (check_shape(B, N, H, D) != SAGE_OK) return 0;
+  return sage::v_workspace(B, N, H, D).bytes;
+}
+
+int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+                           int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
+                           const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                           const float* k_scale, const uint16_t* k_mean, const void* workspace,
+                           size_t workspace_bytes) {
+  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !workspace)
+    return SAGE_ERR_NULL;
+  int st = check_shape(B, N, H, D);
+  if (st != SAGE_OK) return st;
+  if ((st = check_strides(B, N, H, q_sb, q_sn, q_sh)) != SAGE_OK) return st;
+  if ((st = check_strides(B, N, H, k_sb, k_sn, k_sh)) != SAGE_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
+      !aligned16(k_mean) || !aligned16(workspace) || ((uintptr_t)q_scale & 3u) ||
+      ((uintptr_t)k_scale & 3u))
+    return SAGE_ERR_ALIGN;
+  const size_t need = sage::qk_workspace(B, N, H, D).bytes;
+  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
+  const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / 32) * 4),
+                         range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / 64) * 4),
+                         range_of(k_mean, bh * D * 2), range_of(workspace, need)};
+  const Range ins[2] = {range_of(q, view_bytes(B, N, H, D, q_sb, q_sn, q_sh)),
+                        range_of(k, view_bytes(B, N, H, D, k_sb, k_sn, k_sh))};
+  if (any_overlap(outs, 6, ins, 2)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_validate_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
+                          int H, int D, const uint8_t* v_fp8, const float* v_scale,
+                          const float* v_mean, const void* workspace, size_t workspace_bytes) {
+  if (!v || !v_fp8 || !v_scale || !v_mean || !workspace) return SAGE_ERR_NULL;
+  int st = check_shape(B, N, H, D);
+  if (st != SAGE_OK) return st;
+  if ((st = check_strides(B, N, H, v_sb, v_sn, v_sh)) != SAGE_OK) return st;
+  if (!aligned16(v) || !aligned16(v_fp8) || !aligned16(workspace) || ((uintptr_t)v_scale & 3u) ||
+      ((uintptr_t)v_mean & 3u))
+    return SAGE_ERR_ALIGN;
+  const size_t need = sage::v_workspace(B, N, H, D).bytes;
+  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
+  const Range outs[4] = {range_of(v_fp8, bh * D * Np), range_of(v_scale, bh * D * 4),
+                         range_of(v_mean, bh * D * 4), range_of(workspace, need)};
+  const Range ins[1] = {range_of(v, view_bytes(B, N, H, D, v_sb, v_sn, v_sh))};
+  if (any_overlap(outs, 4, ins, 1)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                           const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                           const float* v_mean, int B, int N, int H, int D, const void* out,
+                           int64_t o_sb, int64_t o_sn, int64_t o_sh) {
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !v_mean || !out)
+    return SAGE_ERR_NULL;
+  int st = check_shape(B, N, H, D);
+  if (st != SAGE_OK) return st;
+  if ((st = check_strides(B, N, H, o_sb, o_sn, o_sh)) != SAGE_OK) return st;
+  if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_fp8) || !aligned16(out) ||
+      ((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u) ||
+      ((uintptr_t)v_mean & 3u))
+    return SAGE_ERR_ALIGN;
+  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
+  const Range outs[1] = {range_of(out, view_bytes(B, N, H, D, o_sb, o_sn, o_sh))};
+  const Range ins[7] = {range_of(q_i8, bh * Np * D),      range_of(q_scale, bh * (Np / 32) * 4),
+                        range_of(k_i8, bh * Np * D),      range_of(k_scale, bh * (Np / 64) * 4),
+                        range_of(v_fp8, bh * D * Np),     range_of(v_scale, bh * D * 4),
+                        range_of(v_mean, bh * D * 4)};
+  if (any_overlap(outs, 1, ins, 7)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+                  int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
+                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = sage_validate_quant_qk(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8,
+                                        q_scale, k_i8, k_scale, k_mean, workspace, workspace_bytes);
+  if (st != SAGE_OK) return st;
+  return status_of(sage::launch_quant_qk((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
+                                         (const uint16_t*)k, B > 1 ? k_sb : 0, k_sn,
+                                         H > 1 ? k_sh : 0, B, N, H, D, q_i8, q_scale, k_i8, k_scale,
+                                         k_mean, workspace, (hipStream_t)stream));
+}
+
+int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N, int H, int D,
+                 uint8_t* v_fp8, float* v_scale, float* v_mean, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const int st = sage_validate_quant_v(v, v_sb, v_sn, v_sh, B, N, H, D, v_fp8, v_scale, v_mean,
+                                       workspace, workspace_bytes);
+  if (st != SAGE_OK) return st;
+  return status_of(sage::launch_quant_v((const uint16_t*)v, B > 1 ? v_sb : 0, v_sn, H > 1 ? v_sh : 0,
+                                        B, N, H, D, v_fp8, v_scale, v_mean, workspace,
+                                        (hipStream_t)stream));
+}
+
+int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                  const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                  const float* v_mean, int B, int N, int H, int D, float sm_scale, void* out,
+                  int64_t o_sb, int64_t o_sn, int64_t o_sh, void* stream) {
+  const int st = sage_validate_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N,
+                                        H, D, out, o_sb, o_sn, o_sh);
+  if (st != SAGE_OK) return st;
+  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / __builtin_sqrtf((float)D);
+  return status_of(sage::launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N,
+                                         H, D, sm_scale, (uint16_t*)out, B > 1 ? o_sb : 0, o_sn,
+                                         H > 1 ? o_sh : 0, (hipStream_t)stream));
+}
+
+const char* sage_status_string(int status) {
+  switch (status) {
+    case SAGE_OK: return "ok";
+    case SAGE_ERR_NULL: return "a required pointer is NULL";
+    case SAGE_ERR_SHAPE: return "B, N or H < 1, or B*H*Np*D >= 2^31";
+    case SAGE_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 64 or 128)";
+    case SAGE_ERR_STRIDE: return "a stride of a dimension longer than 1 is not positive";
+    case SAGE_ERR_ALIGN: return "a pointer or stride breaks 16-byte alignment";
+    case SAGE_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case SAGE_ERR_OVERLAP: return "an output overlaps an input or another output";
+    case SAGE_ERR_HIP: return "a HIP launch or runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Host-side internals of libsage: workspace layout and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sage {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t padded_tokens(int64_t N) { return ceil_div(N, 64) * 64; }
+
+// Token chunks per (b, h) for the channel-statistics pass: enough workgroups
+// to cover the 256 CUs several times, never a chunk shorter than 64 tokens.
+struct StatsSplit {
+  int nchunk;
+  int rows_per_chunk;
+};
+inline StatsSplit stats_split(int B, int N, int H) {
+  int64_t bh = (int64_t)B * H;
+  int64_t want = ceil_div(1024, bh);
+  int64_t maxc = ceil_div(N, 64);
+  if (want > maxc) want = maxc;
+  if (want < 1) want = 1;
+  int rpc = (int)ceil_div(N, want);
+  return StatsSplit{(int)ceil_div(N, rpc), rpc};
+}
+
+// sage_quant_qk workspace: fp64 partial sums [BH][nchunk][D].
+struct QkWorkspace {
+  size_t partial_off, bytes;
+};
+inline QkWorkspace qk_workspace(int B, int N, int H, int D) {
+  StatsSplit s = stats_split(B, N, H);
+  size_t bh = (size_t)B * H;
+  QkWorkspace w;
+  w.partial_off = 0;
+  w.bytes = align256(bh * s.nchunk * D * sizeof(double));
+  return w;
+}
+
+// sage_quant_v workspace: fp64 partial sums, fp32 partial min and max
+// [BH][nchunk][D], per-channel 448/a [BH][D].
+struct VWorkspace {
+  size_t sum_off, min_off, max_off, inv_off, bytes;
+};
+inline VWorkspace v_workspace(int B, int N, int H, int D) {
+  StatsSplit s = stats_split(B, N, H);
+  size_t bh = (size_t)B * H, n = bh * s.nchunk * D;
+  VWorkspace w;
+  w.sum_off = 0;
+  w.min_off = align256(n * sizeof(double));
+  w.max_off = w.min_off + align256(n * sizeof(float));
+  w.inv_off = w.max_off + align256(n * sizeof(float));
+  w.bytes = w.inv_off + align256(bh * D * sizeof(float));
+  return w;
+}
+
+hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                           const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                           int B, int N, int H, int D, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                           float* k_scale, uint16_t* k_mean, void* workspace, hipStream_t stream);
+
+hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
+                          int H, int D, uint8_t* v_fp8, float* v_scale, float* v_mean,
+                          void* workspace, hipStream_t stream);
+
+hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                           const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                           const float* v_mean, int B, int N, int H, int D, float sm_scale,
+                           uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                           hipStream_t stream);
+
+}  // namespace sage

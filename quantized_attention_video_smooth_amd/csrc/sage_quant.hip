@@ -1,0 +1,395 @@
+// Quantisation kernels of libsage (gfx950): K smoothing + INT8 K, INT8 Q,
+// V smoothing + FP8 E4M3 V with transpose, zero padding and token permutation.
+//
+// Method: "FLUX.3 Action RTX 5090 report", §02 stage 03 (per-block INT8 QK,
+// FP8 PV, K and V smoothing) and card A (the K centring is done inside the
+// quantiser, keeping the BF16 rounding of K - mean); card C (V is transposed,
+// padded and permuted in one tiled pass; its mean, scale and quantisation are
+// kept).  E4M3 layout per "Why can an A10 run FLUX.1", §1.1.
+//
+// All of this is HBM-bound streaming work.  Each tensor is read twice: once
+// for the per-channel statistics (fp64 sums, and min / max for V) and once to
+// quantise.  The statistics pass splits every (b, h) into token chunks and
+// writes per-chunk partials; a small per-head kernel reduces them in a fixed
+// order and writes the head's mean (and V's scale).  fp64 sums of bf16 values
+// are exact under the condition stated in sage.h, so the mean bits do not
+// depend on the summation order.
+#include <hip/hip_runtime.h>
+
+#include "sage_device.h"
+#include "sage_internal.h"
+
+namespace sage {
+
+namespace {
+
+// Storage slot of token t (0..63) inside a 64-token block of transposed V:
+// slot bits (5..0) = token bits (2, 5, 4, 3, 1, 0).  With this order the 32
+// probabilities one lane holds after the 32x32 INT8 S^T MFMAs (keys
+// 8*(i/4) + 4*half + i%4 of each 32-key half-tile) line up with the 32 bytes
+// that lane supplies to the FP8 PV MFMA.
+__device__ __forceinline__ int v_slot(int t) {
+  return (((t >> 2) & 1) << 5) | (((t >> 5) & 1) << 4) | (((t >> 3) & 3) << 2) | (t & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Channel statistics: grid (nchunk, B*H), 256 threads.  Each thread owns 8
+// consecutive channels (one 16-byte load per token row); D/8 threads cover a
+// row, so a pass reads 256/(D/8) rows.
+// ---------------------------------------------------------------------------
+template <int D, bool IS_V>
+__global__ __launch_bounds__(kThreads) void stats_kernel(
+    const uint16_t* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, int H, int N, int nchunk,
+    int rows_per_chunk, double* __restrict__ psum, float* __restrict__ pmin,
+    float* __restrict__ pmax) {
+  constexpr int LPR = D / 8;
+  constexpr int RPP = kThreads / LPR;
+  __shared__ double s_sum[RPP][D];
+  __shared__ float s_min[IS_V ? RPP : 1][D];
+  __shared__ float s_max[IS_V ? RPP : 1][D];
+
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x, lr = tid / LPR, lc = tid - lr * LPR;
+  const uint16_t* base = x + (int64_t)b * sb + (int64_t)h * sh + lc * 8;
+  const int r0 = c * rows_per_chunk;
+  const int r1 = min(N, r0 + rows_per_chunk);
+
+  double acc[8];
+  float mn[8], mx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    acc[j] = 0.0;
+    mn[j] = __builtin_inff();
+    mx[j] = -__builtin_inff();
+  }
+  auto take = [&](const uint4& v) {
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] += (double)f[j];
+      if (IS_V) {
+        mn[j] = fminf(mn[j], f[j]);
+        mx[j] = fmaxf(mx[j], f[j]);
+      }
+    }
+  };
+  int r = r0 + lr;
+  for (; r + 3 * RPP < r1; r += 4 * RPP) {
+    uint4 v0 = *(const uint4*)(base + (int64_t)r * sn);
+    uint4 v1 = *(const uint4*)(base + (int64_t)(r + RPP) * sn);
+    uint4 v2 = *(const uint4*)(base + (int64_t)(r + 2 * RPP) * sn);
+    uint4 v3 = *(const uint4*)(base + (int64_t)(r + 3 * RPP) * sn);
+    take(v0);
+    take(v1);
+    take(v2);
+    take(v3);
+  }
+  for (; r < r1; r += RPP) take(*(const uint4*)(base + (int64_t)r * sn));
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s_sum[lr][lc * 8 + j] = acc[j];
+    if (IS_V) {
+      s_min[lr][lc * 8 + j] = mn[j];
+      s_max[lr][lc * 8 + j] = mx[j];
+    }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)bh * nchunk + c) * D;
+  if (tid < D) {
+    double s = 0.0;
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+    for (int i = 0; i < RPP; ++i) {
+      s += s_sum[i][tid];
+      if (IS_V) {
+        lo = fminf(lo, s_min[i][tid]);
+        hi = fmaxf(hi, s_max[i][tid]);
+      }
+    }
+    psum[pbase + tid] = s;
+    if (IS_V) {
+      pmin[pbase + tid] = lo;
+      pmax[pbase + tid] = hi;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-head finalisation: grid (B*H), D threads.  Reduces the chunk partials in
+// ascending chunk order; K: k_mean = bf16(fp32(sum / N)); V: v_mean, v_scale
+// and 448/a (kept in the workspace for the quantisation pass).
+// ---------------------------------------------------------------------------
+template <int D, bool IS_V>
+__global__ __launch_bounds__(D) void finalize_kernel(
+    const double* __restrict__ psum, const float* __restrict__ pmin, const float* __restrict__ pmax,
+    int N, int nchunk, uint16_t* __restrict__ k_mean, float* __restrict__ v_mean,
+    float* __restrict__ v_scale, float* __restrict__ v_inv) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  double s = 0.0;
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  for (int c = 0; c < nchunk; ++c) {
+    const size_t o = ((size_t)bh * nchunk + c) * D + d;
+    s += psum[o];
+    if (IS_V) {
+      lo = fminf(lo, pmin[o]);
+      hi = fmaxf(hi, pmax[o]);
+    }
+  }
+  const float mean = (float)(s / (double)N);
+  if (!IS_V) {
+    k_mean[(size_t)bh * D + d] = (uint16_t)bf16_bits_rne(mean);
+  } else {
+    const float a = fmaxf(fabsf(hi - mean), fabsf(lo - mean));
+    const float inv = 448.0f / a;
+    const bool zero = (a == 0.0f) || !__builtin_isfinite(inv);
+    v_mean[(size_t)bh * D + d] = mean;
+    v_scale[(size_t)bh * D + d] = zero ? 0.0f : a / 448.0f;
+    v_inv[(size_t)bh * D + d] = zero ? 0.0f : inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused K centre + BF16 round + INT8 (z = 0) and Q INT8 (z = 1).
+// grid (Np/64, B*H, 2), 256 threads; one 64-token x D tile per workgroup
+// (one K block, or two 32-token Q blocks).  Outputs are head-major [B,H,Np,D].
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void qk_quant_kernel(
+    const uint16_t* __restrict__ q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+    const uint16_t* __restrict__ k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int H, int N, int Np,
+    const uint16_t* __restrict__ k_mean, int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale) {
+  constexpr int LPR = D / 8;
+  constexpr int RPP = kThreads / LPR;
+  constexpr int PASSES = 64 / RPP;
+  __shared__ float s_red[2][kThreads / 64];
+
+  const int t = blockIdx.x, bh = blockIdx.y;
+  const bool is_q = blockIdx.z != 0;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x, lr = tid / LPR, lc = tid - lr * LPR;
+  const uint16_t* src = is_q ? q + (int64_t)b * q_sb + (int64_t)h * q_sh
+                             : k + (int64_t)b * k_sb + (int64_t)h * k_sh;
+  const int64_t sn = is_q ? q_sn : k_sn;
+  src += lc * 8;
+
+  float mean[8];
+  if (!is_q) {
+    const uint4 m = *(const uint4*)(k_mean + (size_t)bh * D + lc * 8);
+    unpack8(m, mean);
+  }
+
+  float x[PASSES][8];
+  float a_lo = 0.0f, a_hi = 0.0f;  // absmax of rows 0..31 and 32..63 of the tile
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = t * 64 + lr + p * RPP;
+    if (r < N) {
+      const uint4 v = *(const uint4*)(src + (int64_t)r * sn);
+      unpack8(v, x[p]);
+      if (!is_q) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[p][j] = bf16_round_f32(x[p][j] - mean[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[p][j] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[p][j]));
+    if (p < PASSES / 2) a_lo = fmaxf(a_lo, m); else a_hi = fmaxf(a_hi, m);
+  }
+  a_lo = wave_max(a_lo);
+  a_hi = wave_max(a_hi);
+  if ((tid & 63) == 0) {
+    s_red[0][tid >> 6] = a_lo;
+    s_red[1][tid >> 6] = a_hi;
+  }
+  __syncthreads();
+  a_lo = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  a_hi = fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
+  if (!is_q) a_lo = a_hi = fmaxf(a_lo, a_hi);
+
+  float inv[2], scale[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float a = s ? a_hi : a_lo;
+    const float iv = 127.0f / a;
+    const bool zero = (a == 0.0f) || !__builtin_isfinite(iv);
+    inv[s] = zero ? 0.0f : iv;
+    scale[s] = zero ? 0.0f : a / 127.0f;
+  }
+
+  int8_t* dst = (is_q ? q_i8 : k_i8) + ((size_t)bh * Np + t * 64) * D + lc * 8;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int rr = lr + p * RPP;
+    const float iv = inv[p < PASSES / 2 ? 0 : 1];
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w0 |= (uint32_t)(i8_code(x[p][j] * iv) & 0xFF) << (8 * j);
+      w1 |= (uint32_t)(i8_code(x[p][j + 4] * iv) & 0xFF) << (8 * j);
+    }
+    *(uint2*)(dst + (size_t)rr * D) = make_uint2(w0, w1);
+  }
+  if (tid == 0) {
+    if (is_q) {
+      q_scale[(size_t)bh * (Np / 32) + 2 * t] = scale[0];
+      q_scale[(size_t)bh * (Np / 32) + 2 * t + 1] = scale[1];
+    } else {
+      k_scale[(size_t)bh * (Np / 64) + t] = scale[0];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V centre + scale + E4M3, transposed to [B,H,D,Np] with the slot permutation.
+// grid (ceil(Np/128), B*H), 256 threads; one 128-token x D tile per workgroup.
+// Each thread converts 4 consecutive tokens x 8 channels (4 consecutive tokens
+// land in 4 consecutive slots) and writes one 32-bit word per channel into an
+// LDS tile [D][128]; the tile is then stored as 16-byte row chunks.  The LDS
+// column chunk is XOR-swizzled by (row / 8) to spread banks.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void v_quant_kernel(
+    const uint16_t* __restrict__ v, int64_t sb, int64_t sn, int64_t sh, int H, int N, int Np,
+    const float* __restrict__ v_mean, const float* __restrict__ v_inv, uint8_t* __restrict__ v_fp8) {
+  constexpr int CPR = D / 8;                     // 8-channel chunks per token row
+  constexpr int MT = (32 * CPR) / kThreads;      // micro-tiles per thread
+  constexpr int LROW = 128;                      // LDS bytes per channel row
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * LROW];
+
+  const int u = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x;
+  const int tok0 = u * 128;
+  const uint16_t* src = v + (int64_t)b * sb + (int64_t)h * sh;
+
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int idx = tid + kThreads * m;
+    const int cc = idx % CPR, g = idx / CPR;  // channel chunk, 4-token group (0..31)
+    const int ch0 = cc * 8;
+    float mu[8], iv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mu[j] = v_mean[(size_t)bh * D + ch0 + j];
+      iv[j] = v_inv[(size_t)bh * D + ch0 + j];
+    }
+    float x[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tok0 + 4 * g + r;
+      if (tok < N) {
+        unpack8(*(const uint4*)(src + (int64_t)tok * sn + ch0), x[r]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float y = (x[r][j] - mu[j]) * iv[j];
+          y = fminf(fmaxf(y, -448.0f), 448.0f);
+          x[r][j] = (iv[j] == 0.0f) ? 0.0f : y;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[r][j] = 0.0f;
+      }
+    }
+    const int col = 64 * (g >> 4) + v_slot((4 * g) & 63);  // multiple of 4
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0][j], x[1][j], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2][j], x[3][j], w, true);
+      const int row = ch0 + j;
+      const int chunk = (col >> 4) ^ ((row >> 3) & 7);
+      *(uint32_t*)(tile + row * LROW + chunk * 16 + (col & 15)) = (uint32_t)w;
+    }
+  }
+  __syncthreads();
+  constexpr int CHUNKS = D * (LROW / 16);
+#pragma unroll
+  for (int i = 0; i < CHUNKS / kThreads; ++i) {
+    const int c = tid + kThreads * i;
+    const int row = c >> 3, c16 = c & 7;
+    const int colg = tok0 + c16 * 16;
+    if (colg < Np) {
+      const uint4 val = *(const uint4*)(tile + row * LROW + ((c16 ^ ((row >> 3) & 7)) * 16));
+      *(uint4*)(v_fp8 + ((size_t)bh * D + row) * Np + colg) = val;
+    }
+  }
+}
+
+template <int D>
+hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                         const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
+                         int H, int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                         uint16_t* k_mean, void* ws, hipStream_t stream) {
+  const StatsSplit s = stats_split(B, N, H);
+  const QkWorkspace w = qk_workspace(B, N, H, D);
+  char* wsb = (char*)ws;
+  const int Np = (int)padded_tokens(N);
+  hipLaunchKernelGGL((stats_kernel<D, false>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream, k,
+                     k_sb, k_sn, k_sh, H, N, s.nchunk, s.rows_per_chunk,
+                     (double*)(wsb + w.partial_off), (float*)nullptr, (float*)nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((finalize_kernel<D, false>), dim3(B * H), dim3(D), 0, stream,
+                     (const double*)(wsb + w.partial_off), (const float*)nullptr,
+                     (const float*)nullptr, N, s.nchunk, k_mean, (float*)nullptr, (float*)nullptr,
+                     (float*)nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((qk_quant_kernel<D>), dim3(Np / 64, B * H, 2), dim3(kThreads), 0, stream, q,
+                     q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, H, N, Np, (const uint16_t*)k_mean, q_i8,
+                     q_scale, k_i8, k_scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t quant_v_impl(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
+                        int H, uint8_t* v_fp8, float* v_scale, float* v_mean, void* ws,
+                        hipStream_t stream) {
+  const StatsSplit s = stats_split(B, N, H);
+  const VWorkspace w = v_workspace(B, N, H, D);
+  char* wsb = (char*)ws;
+  const int Np = (int)padded_tokens(N);
+  float* inv = (float*)(wsb + w.inv_off);
+  hipLaunchKernelGGL((stats_kernel<D, true>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream, v,
+                     v_sb, v_sn, v_sh, H, N, s.nchunk, s.rows_per_chunk,
+                     (double*)(wsb + w.sum_off), (float*)(wsb + w.min_off),
+                     (float*)(wsb + w.max_off));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((finalize_kernel<D, true>), dim3(B * H), dim3(D), 0, stream,
+                     (const double*)(wsb + w.sum_off), (const float*)(wsb + w.min_off),
+                     (const float*)(wsb + w.max_off), N, s.nchunk, (uint16_t*)nullptr, v_mean,
+                     v_scale, inv);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((v_quant_kernel<D>), dim3((Np + 127) / 128, B * H), dim3(kThreads), 0, stream,
+                     v, v_sb, v_sn, v_sh, H, N, Np, (const float*)v_mean, (const float*)inv, v_fp8);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                           const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
+                           int H, int D, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                           float* k_scale, uint16_t* k_mean, void* workspace, hipStream_t stream) {
+  if (D == 128)
+    return quant_qk_impl<128>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_i8, q_scale, k_i8,
+                              k_scale, k_mean, workspace, stream);
+  return quant_qk_impl<64>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_i8, q_scale, k_i8,
+                           k_scale, k_mean, workspace, stream);
+}
+
+hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
+                          int H, int D, uint8_t* v_fp8, float* v_scale, float* v_mean,
+                          void* workspace, hipStream_t stream) {
+  if (D == 128)
+    return quant_v_impl<128>(v, v_sb, v_sn, v_sh, B, N, H, v_fp8, v_scale, v_mean, workspace, stream);
+  return quant_v_impl<64>(v, v_sb, v_sn, v_sh, B, N, H, v_fp8, v_scale, v_mean, workspace, stream);
+}
+
+}  // namespace sage

@@ -1,0 +1,129 @@
+"""Host-only checks of the C ABI: the library loads, exports every function that
+include/sage.h declares, and rejects bad arguments with the documented status
+codes without touching a GPU (sage_validate_*)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+
+@pytest.fixture(scope="module")
+def sage():
+    import quantized_attention_video_smooth_amd as s
+    if not os.path.exists(s.LIB_PATH):
+        from quantized_attention_video_smooth_amd import build
+        build.build()
+    s.lib()
+    return s
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(sage):
+    names = _declared_functions()
+    assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd"} <= set(names)
+    for n in names:
+        assert hasattr(sage.lib(), n), n
+
+
+def test_layout_and_slot_map(sage):
+    import ctypes
+    buf = (ctypes.c_int32 * 4)()
+    assert sage.lib().sage_get_layout(ctypes.addressof(buf)) == 0
+    assert list(buf) == [32, 64, 64, 1]
+    assert sage.lib().sage_get_layout(None) == -1
+    slots = [sage.sage_v_slot(t) for t in range(64)]
+    assert sorted(slots) == list(range(64))
+    assert sage.sage_v_slot(64) == -1 and sage.sage_v_slot(-1) == -1
+    import oracle
+    assert slots == [oracle.v_slot(t) for t in range(64)]
+    assert [sage.sage_padded_tokens(n) for n in (1, 64, 65, 3128, 32760)] == [64, 64, 128, 3136, 32768]
+
+
+A = 1 << 20  # fake, 16-byte aligned "device" addresses spaced far apart
+
+
+def _qk_args(B=1, N=100, H=2, D=64, **over):
+    Np = (N + 63) // 64 * 64
+    a = dict(q=A, q_sb=N * H * D, q_sn=H * D, q_sh=D, k=2 * A, k_sb=N * H * D, k_sn=H * D, k_sh=D,
+             B=B, N=N, H=H, D=D, q_i8=3 * A, q_scale=4 * A, k_i8=5 * A, k_scale=6 * A,
+             k_mean=7 * A, ws=8 * A, ws_bytes=1 << 40)
+    a.update(over)
+    return a
+
+
+def _vqk(sage, a):
+    return sage.lib().sage_validate_quant_qk(a["q"], a["q_sb"], a["q_sn"], a["q_sh"], a["k"], a["k_sb"],
+                                             a["k_sn"], a["k_sh"], a["B"], a["N"], a["H"], a["D"],
+                                             a["q_i8"], a["q_scale"], a["k_i8"], a["k_scale"],
+                                             a["k_mean"], a["ws"], a["ws_bytes"])
+
+
+def test_validate_quant_qk_status_codes(sage):
+    assert _vqk(sage, _qk_args()) == 0
+    assert _vqk(sage, _qk_args(q=None)) == -1
+    assert _vqk(sage, _qk_args(ws=None)) == -1
+    assert _vqk(sage, _qk_args(N=0)) == -2
+    assert _vqk(sage, _qk_args(B=0)) == -2
+    assert _vqk(sage, _qk_args(D=96)) == -3
+    assert _vqk(sage, _qk_args(q_sn=-128)) == -4
+    assert _vqk(sage, _qk_args(k_sn=132)) == -5
+    assert _vqk(sage, _qk_args(q=A + 8)) == -5
+    assert _vqk(sage, _qk_args(ws_bytes=16)) == -6
+    assert _vqk(sage, _qk_args(k_i8=3 * A + 64)) == -7          # overlaps q_i8
+    assert _vqk(sage, _qk_args(q_scale=A + 256)) == -7          # output inside input q
+    assert _vqk(sage, _qk_args(N=1 << 20, H=64, D=128, B=1)) == -2  # >= 2^31 elements
+    # size-1 dimensions may carry any stride
+    assert _vqk(sage, _qk_args(B=1, q_sb=3, k_sb=0)) == 0
+
+
+def test_validate_quant_v_status_codes(sage):
+    lib = sage.lib()
+    ok = (A, 100 * 2 * 64, 2 * 64, 64, 1, 100, 2, 64, 2 * A, 3 * A, 4 * A, 5 * A, 1 << 40)
+    assert lib.sage_validate_quant_v(*ok) == 0
+    bad = list(ok); bad[8] = None
+    assert lib.sage_validate_quant_v(*bad) == -1
+    bad = list(ok); bad[2] = 2 * 64 + 4  # token stride breaks alignment
+    assert lib.sage_validate_quant_v(*bad) == -5
+    bad = list(ok); bad[8] = A + 512     # v_fp8 inside the input
+    assert lib.sage_validate_quant_v(*bad) == -7
+    bad = list(ok); bad[12] = 8
+    assert lib.sage_validate_quant_v(*bad) == -6
+    bad = list(ok); bad[7] = 32
+    assert lib.sage_validate_quant_v(*bad) == -3
+
+
+def test_validate_attn_status_codes(sage):
+    lib = sage.lib()
+    ok = (A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 1, 100, 2, 128, 8 * A, 100 * 2 * 128, 2 * 128, 128)
+    assert lib.sage_validate_attn_fwd(*ok) == 0
+    bad = list(ok); bad[11] = 3 * A + 16   # out overlaps k_i8
+    assert lib.sage_validate_attn_fwd(*bad) == -7
+    bad = list(ok); bad[11] = None
+    assert lib.sage_validate_attn_fwd(*bad) == -1
+    bad = list(ok); bad[13] = 0          # N > 1 with zero token stride
+    assert lib.sage_validate_attn_fwd(*bad) == -4
+
+
+def test_workspace_sizes(sage):
+    assert sage.sage_quant_qk_workspace_size(1, 100, 2, 96) == 0
+    a = sage.sage_quant_qk_workspace_size(2, 4608, 24, 128)
+    b = sage.sage_quant_v_workspace_size(2, 4608, 24, 128)
+    assert 0 < a < b < 64 << 20
+    assert a % 256 == 0 and b % 256 == 0
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    import quantized_attention_video_smooth_amd as s
+    monkeypatch.setattr(s, "_lib", None)
+    monkeypatch.setattr(s, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        s.lib()

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact INT8 Q/K codes, FP8 V codes, all scales and means (padding
+included); attention within relative L2 <= 5e-3 of the oracle's quantised
+tiled path and <= 3e-2 of exact fp64 attention.  On the tiny workload the
+method itself is ~3.6e-2 from exact attention (FP8 rounding of P and V), so
+there the second bar is checked as "no worse than the oracle by more than
+5e-3" and the conflict is recorded.
+"""
+import hashlib
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_ORACLE = 5e-3
+TOL_EXACT = 3e-2
+
+
+def _log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_attention_video_smooth_amd as s
+    s.lib()  # raises if the library is missing
+    return s
+
+
+def _gpu_quant(sage, q, k, v):
+    dev = torch.device("cuda")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    qk = sage.quant_qk(qd, kd)
+    vq = sage.quant_v(vd)
+    torch.cuda.synchronize()
+    return qd, kd, vd, qk, vq
+
+
+def _check_quant_bits(qk, vq, ref_qk, ref_v, N):
+    q_i8, q_scale, k_i8, k_scale, k_mean = [t.cpu() for t in qk]
+    v_fp8, v_scale, v_mean = [t.cpu() for t in vq]
+    nq, nk = math.ceil(N / 32), math.ceil(N / 64)
+    np.testing.assert_array_equal(q_i8[:, :, :N].numpy(), ref_qk["q_i8"])
+    np.testing.assert_array_equal(k_i8[:, :, :N].numpy(), ref_qk["k_i8"])
+    assert torch.all(q_i8[:, :, N:] == 0) and torch.all(k_i8[:, :, N:] == 0)
+    np.testing.assert_array_equal(q_scale[:, :, :nq].numpy().view(np.uint32), ref_qk["q_scale"].view(np.uint32))
+    assert torch.all(q_scale[:, :, nq:] == 0)
+    np.testing.assert_array_equal(k_scale[:, :, :nk].numpy().view(np.uint32), ref_qk["k_scale"].view(np.uint32))
+    np.testing.assert_array_equal(k_mean.view(torch.int16).numpy().view(np.uint16), ref_qk["k_mean"])
+    np.testing.assert_array_equal(v_fp8.numpy(), ref_v["v_fp8"])
+    np.testing.assert_array_equal(v_scale.numpy().view(np.uint32), ref_v["v_scale"].view(np.uint32))
+    np.testing.assert_array_equal(v_mean.numpy().view(np.uint32), ref_v["v_mean"].view(np.uint32))
+
+
+def _rows_gathered(out_nhd, rows):
+    # out [B,N,H,D] -> [B,H,len(rows),D] fp64
+    return out_nhd.float().cpu()[:, rows].permute(0, 2, 1, 3).double().numpy()
+
+
+SMALL = [
+    synth.config(0),
+    synth.custom(1, 1, 2, 64, tag=301),
+    synth.custom(2, 63, 3, 64, tag=302),
+    synth.custom(1, 65, 2, 128, tag=303),
+    synth.custom(3, 200, 2, 128, tag=304),
+    synth.custom(1, 777, 4, 128, tag=305),
+    synth.custom(2, 1000, 1, 64, tag=306),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"{c.name}-B{c.B}N{c.N}H{c.H}D{c.D}")
+def test_small_shapes_full(sage, cfg):
+    _log(f"[parity] {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+    torch.cuda.synchronize()
+    got = _rows_gathered(out, np.arange(cfg.N))
+    tiled = oracle.attn_tiled(ref_qk, ref_v)
+    exact = oracle.attn_exact(q, k, v)
+    e_or, e_ex, e_me = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact), oracle.rel_l2(tiled, exact)
+    _log(f"  rel L2: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}  oracle-vs-exact {e_me:.3e}")
+    assert e_or <= TOL_ORACLE
+    if cfg.N == 1:
+        np.testing.assert_array_equal(got, exact.astype(np.float32).astype(np.float64))
+    assert e_ex <= max(TOL_EXACT, e_me + TOL_ORACLE)
+
+
+WORKLOADS = [1, 2]
+
+
+@pytest.mark.parametrize("idx", WORKLOADS)
+def test_workload_quant_bits_and_attention(sage, idx):
+    cfg = synth.config(idx)
+    _log(f"[parity] workload {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+    torch.cuda.synchronize()
+    rows = synth.query_subset(cfg.N, every=16)
+    got = _rows_gathered(out, rows)
+    tiled = oracle.attn_tiled(ref_qk, ref_v, rows=rows)
+    exact = oracle.attn_exact(q, k, v, rows=rows)
+    e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
+    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}  "
+         f"oracle-vs-exact {oracle.rel_l2(tiled, exact):.3e}")
+    assert e_or <= TOL_ORACLE and e_ex <= TOL_EXACT
+    assert torch.isfinite(out.float()).all()
+
+
+def test_long_workload_sampled(sage):
+    """Long T2V shape (B1 H40 N32760 D128): quantised outputs bit-exact in full;
+    attention on sampled query rows of every head."""
+    cfg = synth.config(3)
+    _log(f"[parity] workload {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+    torch.cuda.synchronize()
+    nb = math.ceil(cfg.N / 32)
+    blocks = [0, nb // 3, (2 * nb) // 3, nb - 1]
+    rows = np.array([r for b in blocks for r in range(32 * b, min(cfg.N, 32 * b + 32))], np.int32)
+    got = _rows_gathered(out, rows)
+    tiled = oracle.attn_tiled(ref_qk, ref_v, rows=rows)
+    exact = oracle.attn_exact(q, k, v, rows=rows)
+    e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
+    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}")
+    assert e_or <= TOL_ORACLE and e_ex <= TOL_EXACT
+
+
+def test_quant_long_bits(sage):
+    """Standalone quant shape (B1 H40 N32760 D128, offsets N(0,4) on Q, K and V)."""
+    cfg = synth.config(4)
+    _log(f"[parity] workload {cfg.name} quant only")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+
+
+def test_strided_v_alias_and_strided_out(sage):
+    """V read as a column slice of a wider projection output; output written into
+    a wider buffer."""
+    cfg = synth.custom(2, 300, 3, 128, tag=307)
+    _log("[parity] strided V / out")
+    q, k, v = synth.make_qkv(cfg)
+    B, N, H, D = q.shape
+    wide = torch.zeros(B, N, H * D + 256, dtype=torch.bfloat16)
+    wide[:, :, 128:128 + H * D] = v.reshape(B, N, H * D)
+    wide_d = wide.cuda()
+    v_view = wide_d[:, :, 128:128 + H * D].view(B, N, H, D)
+    vq = sage.quant_v(v_view)
+    vq_ref = sage.quant_v(v.cuda())
+    torch.cuda.synchronize()
+    for a, b in zip(vq, vq_ref):
+        assert torch.equal(a, b)
+    ref_v = oracle.quant_v(wide[:, :, 128:128 + H * D].view(B, N, H, D))
+    np.testing.assert_array_equal(vq[0].cpu().numpy(), ref_v["v_fp8"])
+    qk = sage.quant_qk(q.cuda(), k.cuda())
+    obuf = torch.zeros(B, N, H * D + 64, dtype=torch.bfloat16, device="cuda")
+    o_view = obuf[:, :, 64:].view(B, N, H, D)
+    sage.attn_fwd(*qk[:4], *vq, N=N, out=o_view)
+    o_ref = sage.attn_fwd(*qk[:4], *vq, N=N)
+    torch.cuda.synchronize()
+    assert torch.equal(o_view, o_ref)
+    assert torch.all(obuf[:, :, :64] == 0)
+
+
+def test_determinism_sha256(sage):
+    cfg = synth.config(2)
+    _log("[parity] determinism x3")
+    q, k, v = (t.cuda() for t in synth.make_qkv(cfg))
+    digests = set()
+    for _ in range(3):
+        qk = sage.quant_qk(q, k)
+        vq = sage.quant_v(v)
+        out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+        torch.cuda.synchronize()
+        h = hashlib.sha256()
+        for t in (*qk, *vq, out):
+            h.update(t.contiguous().view(torch.uint8).cpu().numpy().tobytes())
+        digests.add(h.hexdigest())
+    assert len(digests) == 1
+
+
+def test_sm_scale_argument(sage):
+    cfg = synth.custom(1, 130, 2, 64, tag=308)
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    qk = sage.quant_qk(q.cuda(), k.cuda())
+    vq = sage.quant_v(v.cuda())
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N, sm_scale=0.05)
+    torch.cuda.synchronize()
+    got = _rows_gathered(out, np.arange(cfg.N))
+    assert oracle.rel_l2(got, oracle.attn_tiled(ref_qk, ref_v, sm_scale=0.05)) <= TOL_ORACLE
+
+
+def test_errors_enqueue_nothing(sage):
+    q = torch.zeros(1, 64, 2, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sage.SageError) as e:
+        sage.quant_qk(q, q)
+    assert e.value.status == -3

@@ -3,24 +3,33 @@
 // Method: "FLUX.3 Action RTX 5090 report", §02 stage 03 (INT8 QK, FP8 PV,
 // FP32 accumulation, V smoothing kept) and "MiniMax H3 on DGX Spark", §01
 // (QK INT8 / PV FP8).  The pages give no kernel design for this chip; this one
-// is built around the CDNA4 32x32 MFMA tiles:
+// is built around the CDNA4 32x32 MFMA tiles and the measured cost of the
+// softmax on the vector ALU (per 64-key tile a wave issues 512 cycles of MFMA
+// but roughly twice that of VALU work):
 //
-//   * a workgroup = 4 waves = 128 queries of one (b, h); a wave owns 32
+//   * a workgroup = 8 waves = 256 queries of one (b, h); a wave owns 32
 //     queries, which is exactly one Q quantisation block, so q_scale is a
 //     per-wave scalar;
 //   * the key loop walks 64-key tiles (one K quantisation block, so k_scale is
-//     a per-tile scalar), staged through LDS with double buffering;
+//     a per-tile scalar) through an LDS ring filled with direct global->LDS
+//     loads (no VGPR staging) two tiles ahead, in an XOR-swizzled layout that
+//     keeps the MFMA operand reads free of bank conflicts;
 //   * S^T = K Q^T with v_mfma_i32_32x32x32_i8 (exact int32).  In that layout
 //     lane l holds 32 scores of query l%32, so the row max, the exponentials
 //     and the row sum are lane-local except for one exchange between the two
-//     32-lane halves;
+//     32-lane halves (v_permlane32_swap);
 //   * the probabilities are converted to E4M3 in registers (v_cvt_pk_fp8_f32)
 //     and used directly as the B operand of O^T = V^T P^T with
 //     v_mfma_f32_32x32x64_f8f6f4; V is stored with the slot permutation that
 //     makes those bytes line up (sage_v_slot in sage.h);
-//   * exp2 with log2(e) and the static P scale 448 folded into one FMA;
-//     the rescale of the accumulator is skipped when no row max moved.
+//   * software pipelining: S^T of tile t+1 is issued to the matrix cores before
+//     the softmax of tile t runs on the vector ALU, so the two overlap within
+//     a wave and across the two waves that share each SIMD;
+//   * exp2 with log2(e) and the static P scale 448 folded into one FMA; the
+//     accumulator rescale is skipped when no row max moved.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "sage_device.h"
 #include "sage_internal.h"
@@ -30,31 +39,60 @@ namespace sage {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8]; a field at its maximum does not wait).
+constexpr int kWaitAll = 0;
+template <int VM>
+constexpr int kWaitLgkm0VmCpt = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
 constexpr float kLog2_448 = 8.807354922057604f;  // log2(448)
 
 template <int D>
 struct AttnCfg {
+  static constexpr int NW = 8;               // waves per workgroup
+  static constexpr int NT = NW * 64;         // threads per workgroup
+  static constexpr int QT = NW * 32;         // queries per workgroup
   static constexpr int DC = D / 32;          // 32-wide d chunks
-  static constexpr int KROW = D + 16;        // LDS bytes per K row (padded: conflict-free b128 reads)
-  static constexpr int VROW = 64 + 16;       // LDS bytes per V^T row
-  static constexpr int KBYTES = 64 * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KCH = 64 * D / 16;    // 16-byte chunks per K tile
-  static constexpr int VCH = D * 4;          // 16-byte chunks per V tile (64 bytes per row)
-  static constexpr int KPT = KCH / kThreads; // chunks per thread
-  static constexpr int VPT = VCH / kThreads;
+  static constexpr int JN = D / 16;          // 16-byte chunks per K row
+  static constexpr int KCH = 64 * JN;        // 16-byte chunks per K tile
+  static constexpr int VCH = D * 4;          // 16-byte chunks per V^T tile (64 bytes per row)
+  static constexpr int KBYTES = KCH * 16;
+  static constexpr int STAGE = (KCH + VCH) * 16;
+#ifndef SAGE_ATTN_AHEAD
+#define SAGE_ATTN_AHEAD 2
+#endif
+  static constexpr int AHEAD = SAGE_ATTN_AHEAD;  // tiles loaded ahead of the one in softmax
+  static constexpr int NBUF = AHEAD + 1;         // LDS ring depth (tiles t .. t+AHEAD)
+  static constexpr int CPT = (KCH + VCH) / NT;  // direct-load instructions per wave per tile
+  static_assert(CPT * NT == KCH + VCH, "tile copy must split evenly");
 };
 
+// LDS chunk position (16-byte units) of K row r, chunk j, and of V^T row d,
+// chunk c.  Unpadded rows with the chunk index XOR-swizzled by the row, so that
+// the 16 lanes of each ds_read_b128 pass (16 consecutive rows, one chunk
+// column) hit 16 distinct 16-byte bank groups.
+template <int JN>
+__device__ __forceinline__ int k_pos(int r, int j) { return JN * r + (j ^ ((r / (16 / JN)) % JN)); }
+__device__ __forceinline__ int v_pos(int d, int c) { return 4 * d + (c ^ ((d >> 2) & 3)); }
+
+// max / sum across the two 32-lane halves of a wave (lanes l and l^32).
+__device__ __forceinline__ int xhalf_max(int v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_fp8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, int H, int N, int Np, int n_qtiles, int total_tiles,
     float cq0, uint16_t* __restrict__ out, int64_t o_sb, int64_t o_sn, int64_t o_sh) {
   using C = AttnCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NBUF * C::STAGE];
 
   // XCD-aware mapping: workgroup i runs on XCD i % 8; give each XCD a
   // contiguous run of (head, q-tile) work so a head's K/V stay in one L2.
@@ -64,9 +102,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int bh = logical / n_qtiles, qt = logical - bh * n_qtiles;
   const int b = bh / H, h = bh - b * H;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform values kept in scalar registers (so the tile index, the
+  // k_scale loads and the phase branches are scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const int q0 = qt * 128 + wave * 32;
+  const int q0 = qt * C::QT + wave * 32;
   const int ntiles = Np / 64;
 
   // Q^T operand (B of the S^T MFMA): lane holds query q0+l32, d = 32*dc + 16*half .. +16.
@@ -86,32 +127,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const uint8_t* vbase = v_fp8 + (size_t)bh * D * Np;
   const float* ksc = k_scale + (size_t)bh * ntiles;
 
-  // Per-thread share of one K tile (KPT chunks) and one V^T tile (VPT chunks).
-  uint4 kreg[C::KPT], vreg[C::VPT];
-#define SAGE_GLOAD(t_)                                                                   \
-  do {                                                                                   \
-    _Pragma("unroll") for (int i_ = 0; i_ < C::KPT; ++i_) {                              \
-      const int c_ = tid + kThreads * i_;                                                \
-      kreg[i_] = *(const uint4*)(kbase + (size_t)(t_) * 64 * D + c_ * 16);               \
-    }                                                                                    \
-    _Pragma("unroll") for (int i_ = 0; i_ < C::VPT; ++i_) {                              \
-      const int c_ = tid + kThreads * i_;                                                \
-      vreg[i_] = *(const uint4*)(vbase + (size_t)(c_ >> 2) * Np + (t_) * 64 + (c_ & 3) * 16); \
-    }                                                                                    \
-  } while (0)
-#define SAGE_SSTORE(buf_)                                                                \
-  do {                                                                                   \
-    uint8_t* ks_ = smem + (buf_) * C::STAGE;                                             \
-    uint8_t* vs_ = ks_ + C::KBYTES;                                                      \
-    _Pragma("unroll") for (int i_ = 0; i_ < C::KPT; ++i_) {                              \
-      const int c_ = tid + kThreads * i_;                                                \
-      *(uint4*)(ks_ + (c_ / (D / 16)) * C::KROW + (c_ % (D / 16)) * 16) = kreg[i_];      \
-    }                                                                                    \
-    _Pragma("unroll") for (int i_ = 0; i_ < C::VPT; ++i_) {                              \
-      const int c_ = tid + kThreads * i_;                                                \
-      *(uint4*)(vs_ + (c_ >> 2) * C::VROW + (c_ & 3) * 16) = vreg[i_];                   \
-    }                                                                                    \
-  } while (0)
+  // ---- global -> LDS staging: direct loads (global_load_lds_dwordx4) ----
+  // Instruction i of wave w fills tile chunk positions g = (i*NW + w)*64 + lane
+  // (K positions first, then V^T); every lane fetches the global chunk that
+  // belongs at its LDS position, so the swizzled layout costs nothing here.
+  int goff[C::CPT];  // per-lane global byte offset within a tile (tile term added per load)
+  bool gisv[C::CPT];
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int g = (i * C::NW + wave) * 64 + lane;
+    if (g < C::KCH) {
+      const int r = g / C::JN, jx = g % C::JN;
+      const int j = jx ^ ((r / (16 / C::JN)) % C::JN);
+      goff[i] = r * D + j * 16;
+      gisv[i] = false;
+    } else {
+      const int p = g - C::KCH, d = p >> 2, cx = p & 3;
+      const int c = cx ^ ((d >> 2) & 3);
+      goff[i] = d * Np + c * 16;
+      gisv[i] = true;
+    }
+  }
+  auto gload_lds = [&](int t) __attribute__((always_inline)) {
+    uint8_t* slot = smem + (t % C::NBUF) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int wbase = (i * C::NW + wave) * 64 * 16;  // this wave's LDS bytes in the slot
+      const uint8_t* src = gisv[i] ? (const uint8_t*)vbase + (size_t)t * 64 + goff[i]
+                                   : (const uint8_t*)kbase + (size_t)t * 64 * D + goff[i];
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(slot + wbase), 16, 0, 0);
+    }
+  };
 
   v16f acc[C::DC];
 #pragma unroll
@@ -120,64 +167,63 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     for (int i = 0; i < 16; ++i) acc[dc][i] = 0.0f;
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
+  v8i pop;
+  float ksc_cur = ksc[0];  // k_scale of the tile whose softmax is next
 
-  SAGE_GLOAD(0);
-  SAGE_SSTORE(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    // prefetch the next tile (the last iteration re-reads its own tile; the
-    // other buffer is free then, so the unconditional store below is harmless)
-    SAGE_GLOAD(min(t + 1, ntiles - 1));
-    const uint8_t* ks = smem + buf * C::STAGE;
-    const uint8_t* vs = ks + C::KBYTES;
-
-    // ---- S^T = K Q^T (two 32-key halves of the tile) ----
-    v16i s[2];
+  // S^T(t) = K(t) Q^T into sdst (operands read from LDS slot t % 3).
+  auto qk_mfma = [&](int t, v16i (&sdst)[2]) __attribute__((always_inline)) {
+    const uint8_t* ks = smem + (t % C::NBUF) * C::STAGE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-      const uint8_t* kr = ks + (32 * kb + l32) * C::KROW + 16 * half;
+      sdst[kb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int dc = 0; dc < C::DC; ++dc) {
-        const v4i a = *(const v4i*)(kr + 32 * dc);
-        s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[dc], s[kb], 0, 0, 0);
+        const v4i a = *(const v4i*)(ks + 16 * k_pos<C::JN>(32 * kb + l32, 2 * dc + half));
+        sdst[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[dc], sdst[kb], 0, 0, 0);
       }
     }
-    // key index of s[kb][i] inside the tile: 32*kb + 8*(i/4) + 4*half + i%4
+  };
+  // V^T(t) operands from LDS, and O^T += V^T(t) P^T(t).
+  auto load_v = [&](int t, v8i (&vop)[C::DC]) __attribute__((always_inline)) {
+    const uint8_t* vs = smem + (t % C::NBUF) * C::STAGE + C::KBYTES;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+      const v4i lo = *(const v4i*)(vs + 16 * v_pos(32 * dc + l32, 2 * half));
+      const v4i hi = *(const v4i*)(vs + 16 * v_pos(32 * dc + l32, 2 * half + 1));
+      vop[dc] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  auto pv_mfma = [&](const v8i (&vop)[C::DC]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc)
+      acc[dc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[dc], pop, acc[dc], 0, 0, 0, 0, 0, 0);
+  };
+
+  // Softmax of S^T(t) (in scur): row max, P = exp2(s*c - m) * 448 packed to
+  // E4M3 (byte 16*kb + i of pop), row sum, accumulator rescale.
+  auto softmax = [&](int t, v16i (&scur)[2], auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const float c = cq * ksc_cur;
+    const float ksc_next = ksc[min(t + 1, ntiles - 1)];  // used by the next tile
+    // key index of scur[kb][i] inside the tile: 32*kb + 8*(i/4) + 4*half + i%4
     const int nvalid = N - t * 64;  // keys at or beyond nvalid are padding
-    if (nvalid < 64) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key >= nvalid) s[kb][i] = INT32_MIN;
+          if (key >= nvalid) scur[kb][i] = INT32_MIN;
         }
     }
-    int mxi = s[0][0];
+    int mxi = scur[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mxi = max(mxi, s[kb][i]);
-    mxi = max(mxi, __shfl_xor(mxi, 32, 64));
-
-    const float c = cq * ksc[t];
+      for (int i = 0; i < 16; ++i) mxi = max(mxi, scur[kb][i]);
+    mxi = xhalf_max(mxi);
     const float m_new = fmaxf(m_run, (float)mxi * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    if (__any(m_new != m_run)) {
-      l_run *= alpha;
-#pragma unroll
-      for (int dc = 0; dc < C::DC; ++dc)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dc][i] *= alpha;
-    }
-    m_run = m_new;
     const float bias = kLog2_448 - m_new;
-
-    // ---- P = exp2(s*c - m) * 448, row sum, E4M3 pack (byte 16*kb + i) ----
-    v8i pop;
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -187,8 +233,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[kb][i], c, bias));
-          if (nvalid < 64) {
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf((float)scur[kb][i], c, bias));
+          if constexpr (MASKED) {
             const int key = 32 * kb + 8 * r + 4 * half + e;
             if (key >= nvalid) x = 0.0f;
           }
@@ -199,24 +245,68 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pop[4 * kb + r] = w;
       }
-    l_run += lsum;
-
-    // ---- O^T += V^T P^T ----
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__any(m_new != m_run)) {  // skip when no row max of this wave moved
+      l_run *= alpha;
 #pragma unroll
-    for (int dc = 0; dc < C::DC; ++dc) {
-      const uint8_t* vr = vs + (32 * dc + l32) * C::VROW + 32 * half;
-      const v4i lo = *(const v4i*)(vr);
-      const v4i hi = *(const v4i*)(vr + 16);
-      const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[dc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, acc[dc], 0, 0, 0, 0, 0, 0);
+      for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dc][i] *= alpha;
     }
+    l_run += lsum;
+    m_run = m_new;
+    ksc_cur = ksc_next;
+  };
 
-    SAGE_SSTORE(buf ^ 1);
-    __syncthreads();
+  // One tile: start the direct loads of tile t+AHEAD into the ring slot of
+  // tile t-1 (whose last read, its V, was before the previous barrier), issue
+  // S^T(t+1) on the matrix cores, run the softmax of tile t on the vector ALU
+  // meanwhile, then O^T += V^T(t) P^T(t).  The closing barrier needs this
+  // wave's LDS reads drained (the slot of tile t is refilled next step) and the
+  // loads of tile t+2 landed (read from the next step on); with AHEAD = 3 the
+  // loads of tile t+3 stay in flight across it.  A raw s_barrier is used
+  // because __syncthreads() would always wait for every load.
+  auto step = [&](int t, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag)
+      __attribute__((always_inline)) {
+    const bool issue = t + C::AHEAD < ntiles;
+    if (issue) gload_lds(t + C::AHEAD);
+    if (t + 1 < ntiles) qk_mfma(t + 1, snext);
+    v8i vop[C::DC];
+    load_v(t, vop);
+    softmax(t, scur, masked_tag);
+    pv_mfma(vop);
+    if (issue && C::AHEAD > 2) __builtin_amdgcn_s_waitcnt(kWaitLgkm0VmCpt<C::CPT>);
+    else __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __asm__ volatile("s_barrier" ::: "memory");
+  };
+
+  // ---- prologue: tiles 0, 1 and 2 in LDS, S^T(0) issued ----
+#pragma unroll
+  for (int i = 0; i < C::AHEAD; ++i)
+    if (i < ntiles) gload_lds(i);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();
+  v16i sA[2], sB[2];
+  qk_mfma(0, sA);
+
+  // ---- key loop, unrolled by two so the S buffers alternate statically ----
+  const int nfull = N / 64;  // tiles without padding keys
+  int t = 0;
+  for (; t + 1 < nfull; t += 2) {
+    step(t, sA, sB, std::false_type{});
+    step(t + 1, sB, sA, std::false_type{});
+  }
+  if (t < nfull) {  // t even: S^T(t) is in sA
+    step(t, sA, sB, std::false_type{});
+    ++t;
+  }
+  if (t < ntiles) {  // the last tile holds padding keys
+    if (t & 1) step(t, sB, sA, std::true_type{});
+    else step(t, sA, sB, std::true_type{});
   }
 
   // ---- epilogue: O = acc / (448 * l) * v_scale + v_mean, bf16 NHD ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = xhalf_sum(l_run);
   const float inv_l = 1.0f / l_tot;
   const int qi = q0 + l32;
   if (qi < N) {
@@ -237,8 +327,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         *(uint2*)(orow + d0) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
       }
   }
-#undef SAGE_GLOAD
-#undef SAGE_SSTORE
 }
 
 template <int D>
@@ -247,13 +335,13 @@ hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
                      const float* v_mean, int B, int N, int H, float sm_scale, uint16_t* out,
                      int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
   const int Np = (int)padded_tokens(N);
-  const int n_qtiles = (int)ceil_div(N, 128);
+  const int n_qtiles = (int)ceil_div(N, AttnCfg<D>::QT);
   const int total = B * H * n_qtiles;
   const int grid = (int)ceil_div(total, 8) * 8;
   const float cq0 = sm_scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, q_i8, q_scale,
-                     k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, cq0, out,
-                     o_sb, o_sn, o_sh);
+  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3(grid), dim3(AttnCfg<D>::NT), 0, stream, q_i8,
+                     q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, cq0,
+                     out, o_sb, o_sn, o_sh);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ struct StatsSplit {
 };
 inline StatsSplit stats_split(int B, int N, int H) {
   int64_t bh = (int64_t)B * H;
-  int64_t want = ceil_div(1024, bh);
+  int64_t want = ceil_div(2048, bh);
   int64_t maxc = ceil_div(N, 64);
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;

@@ -76,15 +76,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     }
   };
   int r = r0 + lr;
-  for (; r + 3 * RPP < r1; r += 4 * RPP) {
-    uint4 v0 = *(const uint4*)(base + (int64_t)r * sn);
-    uint4 v1 = *(const uint4*)(base + (int64_t)(r + RPP) * sn);
-    uint4 v2 = *(const uint4*)(base + (int64_t)(r + 2 * RPP) * sn);
-    uint4 v3 = *(const uint4*)(base + (int64_t)(r + 3 * RPP) * sn);
-    take(v0);
-    take(v1);
-    take(v2);
-    take(v3);
+  for (; r + 7 * RPP < r1; r += 8 * RPP) {  // 8 independent 16-byte loads in flight
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const uint4*)(base + (int64_t)(r + u * RPP) * sn);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) take(v[u]);
   }
   for (; r < r1; r += RPP) take(*(const uint4*)(base + (int64_t)r * sn));
 
@@ -129,12 +126,33 @@ __global__ __launch_bounds__(D) void finalize_kernel(
   const int bh = blockIdx.x, d = threadIdx.x;
   double s = 0.0;
   float lo = __builtin_inff(), hi = -__builtin_inff();
-  for (int c = 0; c < nchunk; ++c) {
-    const size_t o = ((size_t)bh * nchunk + c) * D + d;
-    s += psum[o];
+  const size_t base = (size_t)bh * nchunk * D + d;
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8) {  // 8 loads in flight, summed in ascending chunk order
+    double ps[8];
+    float pl[8], ph[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ps[u] = psum[base + (size_t)(c + u) * D];
+      if (IS_V) {
+        pl[u] = pmin[base + (size_t)(c + u) * D];
+        ph[u] = pmax[base + (size_t)(c + u) * D];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s += ps[u];
+      if (IS_V) {
+        lo = fminf(lo, pl[u]);
+        hi = fmaxf(hi, ph[u]);
+      }
+    }
+  }
+  for (; c < nchunk; ++c) {
+    s += psum[base + (size_t)c * D];
     if (IS_V) {
-      lo = fminf(lo, pmin[o]);
-      hi = fmaxf(hi, pmax[o]);
+      lo = fminf(lo, pmin[base + (size_t)c * D]);
+      hi = fmaxf(hi, pmax[base + (size_t)c * D]);
     }
   }
   const float mean = (float)(s / (double)N);
@@ -166,7 +184,10 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
   constexpr int PASSES = 64 / RPP;
   __shared__ float s_red[2][kThreads / 64];
 
-  const int t = blockIdx.x, bh = blockIdx.y;
+  // heads in reverse order: the statistics pass walked them forwards, so the
+  // most recently read heads (most likely still in the memory-side cache)
+  // are re-read first
+  const int t = blockIdx.x, bh = gridDim.y - 1 - blockIdx.y;
   const bool is_q = blockIdx.z != 0;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x, lr = tid / LPR, lc = tid - lr * LPR;
@@ -263,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void v_quant_kernel(
   constexpr int LROW = 128;                      // LDS bytes per channel row
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * LROW];
 
-  const int u = blockIdx.x, bh = blockIdx.y;
+  const int u = blockIdx.x, bh = gridDim.y - 1 - blockIdx.y;  // reverse head order (as above)
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x;
   const int tok0 = u * 128;

@@ -76,6 +76,8 @@ SMALL = [
     synth.custom(3, 200, 2, 128, tag=304),
     synth.custom(1, 777, 4, 128, tag=305),
     synth.custom(2, 1000, 1, 64, tag=306),
+    # 640 heads: more heads than workgroups of one wave of the grid
+    synth.custom(4, 100, 160, 64, tag=309),
 ]
 
 
@@ -221,3 +223,15 @@ def test_errors_enqueue_nothing(sage):
     with pytest.raises(sage.SageError) as e:
         sage.quant_qk(q, q)
     assert e.value.status == -3
+
+
+def test_quant_single_long_head(sage):
+    """One head of 270000 tokens at D=128: every statistics chunk is long and
+    the quantised tensors span 33 MB per head."""
+    cfg = synth.custom(1, 270000, 1, 128, tag=311)
+    _log(f"[parity] long head B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D} quant only")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
+    _, _, _, qk, vq = _gpu_quant(sage, q, k, v)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)

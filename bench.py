@@ -101,6 +101,9 @@ def main():
                     choices=["tiny", "flux_joint", "video_early", "long_t2v", "quant_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the run, copy 256 MiB device to device once: a kernel of known "
+                         "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counter readings")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -187,12 +190,14 @@ def main():
     avg = {k2: sum(v2) / len(v2) for k2, v2 in per.items()}
 
     work = algorithmic(B, N, H, D)
+    waves, wgs = sage.sage_attn_launch_shape(B, N, H, D)
     step_s = ms_per_step * 1e-3
     if do_attn:
         value = work["attn_ops"] / step_s / 1e12
         attn_tflops = work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12
         roofline = {
-            "kernel": "sage_attn_fwd (attn_fwd_kernel<128>)",
+            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}>: {waves}-wave workgroups, "
+                      f"{wgs} per launch)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_MFMA_TFLOPS,
@@ -234,6 +239,13 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
+    if args.copy_calibration:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(res), flush=True)
 
 

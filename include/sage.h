@@ -170,6 +170,15 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale,
                   int B, int N, int H, int D, float sm_scale,
                   void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, void* stream);
 
+/* Launch shape that sage_attn_fwd uses for these sizes on the current device:
+ * waves per workgroup (32 queries each) and workgroups launched.  Eight waves
+ * (256 queries per workgroup, one per CU) when the grid is at least eight such
+ * workgroups per CU deep, else four (128 queries, two per CU: finer load
+ * balance for shallow grids).  Without a device a 256-CU part is assumed.
+ * Returns SAGE_OK, SAGE_ERR_NULL, or the shape status of sage_attn_fwd. */
+int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
+                           int* workgroups);
+
 /* Host-only argument checks of the three entry points: same arguments (less
  * the stream), same status codes, no HIP calls; usable without a GPU. */
 int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,

@@ -51,6 +51,7 @@ _SIGS = {
     "sage_validate_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz], _i32),
     "sage_validate_attn_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                 _vp, _i64, _i64, _i64], _i32),
+    "sage_attn_launch_shape": ([_i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "sage_status_string": ([_i32], ctypes.c_char_p),
 }
 
@@ -95,6 +96,14 @@ def sage_quant_v(*args) -> int:
 
 def sage_attn_fwd(*args) -> int:
     return lib().sage_attn_fwd(*args)
+
+
+def sage_attn_launch_shape(B: int, N: int, H: int, D: int) -> tuple:
+    """(waves per workgroup, workgroups) of the attention launch for these sizes."""
+    w, g = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().sage_attn_launch_shape(B, N, H, D, ctypes.byref(w), ctypes.byref(g)),
+           "sage_attn_launch_shape")
+    return w.value, g.value
 
 
 def sage_padded_tokens(n: int) -> int:

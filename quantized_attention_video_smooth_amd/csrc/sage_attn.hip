@@ -7,12 +7,13 @@
 // softmax on the vector ALU (per 64-key tile a wave issues 512 cycles of MFMA
 // but roughly twice that of VALU work):
 //
-//   * a workgroup = 8 waves = 256 queries of one (b, h); a wave owns 32
-//     queries, which is exactly one Q quantisation block, so q_scale is a
-//     per-wave scalar;
+//   * a workgroup = 8 waves (256 queries) or 4 waves (128 queries, two
+//     workgroups per CU, chosen when the grid is shallow) of one (b, h); a
+//     wave owns 32 queries, which is exactly one Q quantisation block, so
+//     q_scale is a per-wave scalar;
 //   * the key loop walks 64-key tiles (one K quantisation block, so k_scale is
 //     a per-tile scalar) through an LDS ring filled with direct global->LDS
-//     loads (no VGPR staging) two tiles ahead, in an XOR-swizzled layout that
+//     loads (no VGPR staging) two or three tiles ahead, in an XOR-swizzled layout that
 //     keeps the MFMA operand reads free of bank conflicts;
 //   * S^T = K Q^T with v_mfma_i32_32x32x32_i8 (exact int32).  In that layout
 //     lane l holds 32 scores of query l%32, so the row max, the exponentials
@@ -29,6 +30,7 @@
 //     accumulator rescale is skipped when no row max moved.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "sage_device.h"
@@ -46,9 +48,12 @@ template <int VM>
 constexpr int kWaitLgkm0VmCpt = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
 constexpr float kLog2_448 = 8.807354922057604f;  // log2(448)
 
-template <int D>
+// NW waves per workgroup.  Eight waves (256 queries) share each K/V tile in
+// LDS best on long grids; four waves (128 queries, two workgroups per CU)
+// give finer load balance when the grid is only a few workgroups per CU deep.
+template <int D, int NW_>
 struct AttnCfg {
-  static constexpr int NW = 8;               // waves per workgroup
+  static constexpr int NW = NW_;             // waves per workgroup
   static constexpr int NT = NW * 64;         // threads per workgroup
   static constexpr int QT = NW * 32;         // queries per workgroup
   static constexpr int DC = D / 32;          // 32-wide d chunks
@@ -57,10 +62,9 @@ struct AttnCfg {
   static constexpr int VCH = D * 4;          // 16-byte chunks per V^T tile (64 bytes per row)
   static constexpr int KBYTES = KCH * 16;
   static constexpr int STAGE = (KCH + VCH) * 16;
-#ifndef SAGE_ATTN_AHEAD
-#define SAGE_ATTN_AHEAD 2
-#endif
-  static constexpr int AHEAD = SAGE_ATTN_AHEAD;  // tiles loaded ahead of the one in softmax
+  // tiles loaded ahead of the one in softmax: two workgroups per CU keep
+  // three in flight within the same LDS budget per CU
+  static constexpr int AHEAD = NW == 8 ? 2 : 3;
   static constexpr int NBUF = AHEAD + 1;         // LDS ring depth (tiles t .. t+AHEAD)
   static constexpr int CPT = (KCH + VCH) / NT;  // direct-load instructions per wave per tile
   static_assert(CPT * NT == KCH + VCH, "tile copy must split evenly");
@@ -84,14 +88,14 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-template <int D>
-__global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_fp8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, int H, int N, int Np, int n_qtiles, int total_tiles,
     float cq0, uint16_t* __restrict__ out, int64_t o_sb, int64_t o_sn, int64_t o_sh) {
-  using C = AttnCfg<D>;
+  using C = AttnCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NBUF * C::STAGE];
 
   // XCD-aware mapping: workgroup i runs on XCD i % 8; give each XCD a
@@ -131,21 +135,22 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
   // Instruction i of wave w fills tile chunk positions g = (i*NW + w)*64 + lane
   // (K positions first, then V^T); every lane fetches the global chunk that
   // belongs at its LDS position, so the swizzled layout costs nothing here.
+  // Whether a wave's instruction i copies V^T (else K) chunks depends on the
+  // wave only (KCH is a multiple of 64), so it is a scalar condition.
+  static_assert(C::KCH % 64 == 0, "K chunks must fill whole waves");
+  auto is_v = [&](int i) __attribute__((always_inline)) { return (i * C::NW + wave) * 64 >= C::KCH; };
   int goff[C::CPT];  // per-lane global byte offset within a tile (tile term added per load)
-  bool gisv[C::CPT];
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
     const int g = (i * C::NW + wave) * 64 + lane;
-    if (g < C::KCH) {
+    if (!is_v(i)) {
       const int r = g / C::JN, jx = g % C::JN;
       const int j = jx ^ ((r / (16 / C::JN)) % C::JN);
       goff[i] = r * D + j * 16;
-      gisv[i] = false;
     } else {
       const int p = g - C::KCH, d = p >> 2, cx = p & 3;
       const int c = cx ^ ((d >> 2) & 3);
       goff[i] = d * Np + c * 16;
-      gisv[i] = true;
     }
   }
   auto gload_lds = [&](int t) __attribute__((always_inline)) {
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int wbase = (i * C::NW + wave) * 64 * 16;  // this wave's LDS bytes in the slot
-      const uint8_t* src = gisv[i] ? (const uint8_t*)vbase + (size_t)t * 64 + goff[i]
+      const uint8_t* src = is_v(i) ? (const uint8_t*)vbase + (size_t)t * 64 + goff[i]
                                    : (const uint8_t*)kbase + (size_t)t * 64 * D + goff[i];
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(slot + wbase), 16, 0, 0);
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
     for (int i = 0; i < 16; ++i) acc[dc][i] = 0.0f;
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
-  v8i pop;
+  v8i pop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   float ksc_cur = ksc[0];  // k_scale of the tile whose softmax is next
 
   // S^T(t) = K(t) Q^T into sdst (operands read from LDS slot t % 3).
@@ -241,10 +246,19 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
           p[e] = x;
           lsum += x;
         }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        // the high half is written next, so the old register serves as the
+        // untouched half (no zeroing move)
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pop[4 * kb + r], false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pop[4 * kb + r] = w;
       }
+    // Keep the exponentials and packs in this basic block, ahead of the
+    // rescale branch (the compiler would sink them past it): there they
+    // share a block with the next tile's S^T MFMAs, and the register
+    // allocation of the loop stays free of spills.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(pop[i]));
+    asm volatile("" : "+v"(lsum));
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     if (__any(m_new != m_run)) {  // skip when no row max of this wave moved
       l_run *= alpha;
@@ -266,11 +280,14 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
   // loads of tile t+2 landed (read from the next step on); with AHEAD = 3 the
   // loads of tile t+3 stay in flight across it.  A raw s_barrier is used
   // because __syncthreads() would always wait for every load.
-  auto step = [&](int t, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag)
+  // next_tag: std::true_type when tile t+1 exists (its S^T MFMAs are issued
+  // here, in the same basic block as the softmax, so the two can interleave),
+  // std::false_type for the last tile.
+  auto step = [&](int t, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag, auto next_tag)
       __attribute__((always_inline)) {
     const bool issue = t + C::AHEAD < ntiles;
     if (issue) gload_lds(t + C::AHEAD);
-    if (t + 1 < ntiles) qk_mfma(t + 1, snext);
+    if constexpr (decltype(next_tag)::value) qk_mfma(t + 1, snext);
     v8i vop[C::DC];
     load_v(t, vop);
     softmax(t, scur, masked_tag);
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
     __asm__ volatile("s_barrier" ::: "memory");
   };
 
-  // ---- prologue: tiles 0, 1 and 2 in LDS, S^T(0) issued ----
+  // ---- prologue: tiles 0 .. AHEAD-1 in LDS, S^T(0) issued ----
 #pragma unroll
   for (int i = 0; i < C::AHEAD; ++i)
     if (i < ntiles) gload_lds(i);
@@ -290,19 +307,25 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
   qk_mfma(0, sA);
 
   // ---- key loop, unrolled by two so the S buffers alternate statically ----
+  // Main loop: pairs of tiles followed by at least one more tile (all such
+  // tiles are full: only the last tile can hold padding).  One or two tiles
+  // remain after it; the last of them is padded when N % 64 != 0.
   const int nfull = N / 64;  // tiles without padding keys
   int t = 0;
-  for (; t + 1 < nfull; t += 2) {
-    step(t, sA, sB, std::false_type{});
-    step(t + 1, sB, sA, std::false_type{});
+  for (; t + 2 < ntiles; t += 2) {
+    step(t, sA, sB, std::false_type{}, std::true_type{});
+    step(t + 1, sB, sA, std::false_type{}, std::true_type{});
   }
-  if (t < nfull) {  // t even: S^T(t) is in sA
-    step(t, sA, sB, std::false_type{});
-    ++t;
-  }
-  if (t < ntiles) {  // the last tile holds padding keys
-    if (t & 1) step(t, sB, sA, std::true_type{});
-    else step(t, sA, sB, std::true_type{});
+  auto last_step = [&](int t, v16i (&scur)[2], v16i (&snext)[2]) __attribute__((always_inline)) {
+    if (t < nfull) step(t, scur, snext, std::false_type{}, std::false_type{});
+    else step(t, scur, snext, std::true_type{}, std::false_type{});
+  };
+  // t is even here: S^T(t) is in sA
+  if (t + 1 < ntiles) {
+    step(t, sA, sB, std::false_type{}, std::true_type{});
+    last_step(t + 1, sB, sA);
+  } else {
+    last_step(t, sA, sB);
   }
 
   // ---- epilogue: O = acc / (448 * l) * v_scale + v_mean, bf16 NHD ----
@@ -329,23 +352,61 @@ __global__ __launch_bounds__(AttnCfg<D>::NT, 1) void attn_fwd_kernel(
   }
 }
 
+template <int D, int NW>
+hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                       const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                       const float* v_mean, int B, int N, int H, float sm_scale, uint16_t* out,
+                       int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
+  using C = AttnCfg<D, NW>;
+  const int Np = (int)padded_tokens(N);
+  const int n_qtiles = (int)ceil_div(N, C::QT);
+  const int total = B * H * n_qtiles;
+  const int grid = (int)ceil_div(total, 8) * 8;
+  const float cq0 = sm_scale * kLog2e;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, q_i8, q_scale,
+                     k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, cq0, out, o_sb,
+                     o_sn, o_sh);
+  return hipGetLastError();
+}
+
+// Eight-wave workgroups when the grid is at least 8 of them per CU deep,
+// else four-wave ones (measured on MI355X: FLUX-sized grids of ~3.4 per CU
+// run ~20% faster with four waves, 20-deep grids ~1% slower).
+int attn_waves(int B, int N, int H) {
+  static std::atomic<int> ncu_cache{0};
+  int ncu = ncu_cache.load(std::memory_order_relaxed);
+  if (ncu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+      ncu = 256;
+    ncu_cache.store(ncu, std::memory_order_relaxed);
+  }
+  const int64_t wg8 = (int64_t)B * H * ceil_div(N, 256);
+  return wg8 >= 8 * (int64_t)ncu ? 8 : 4;
+}
+
 template <int D>
 hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                      const float* v_mean, int B, int N, int H, float sm_scale, uint16_t* out,
                      int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
-  const int Np = (int)padded_tokens(N);
-  const int n_qtiles = (int)ceil_div(N, AttnCfg<D>::QT);
-  const int total = B * H * n_qtiles;
-  const int grid = (int)ceil_div(total, 8) * 8;
-  const float cq0 = sm_scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3(grid), dim3(AttnCfg<D>::NT), 0, stream, q_i8,
-                     q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, cq0,
-                     out, o_sb, o_sn, o_sh);
-  return hipGetLastError();
+  if (attn_waves(B, N, H) == 8)
+    return attn_launch<D, 8>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, sm_scale,
+                             out, o_sb, o_sn, o_sh, stream);
+  return attn_launch<D, 4>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, sm_scale,
+                           out, o_sb, o_sn, o_sh, stream);
 }
 
 }  // namespace
+
+void attn_shape(int B, int N, int H, int D, int* waves, int* workgroups) {
+  (void)D;
+  const int nw = attn_waves(B, N, H);
+  *waves = nw;
+  *workgroups = (int)(ceil_div((int64_t)B * H * ceil_div(N, 32 * nw), 8) * 8);
+}
 
 hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale,

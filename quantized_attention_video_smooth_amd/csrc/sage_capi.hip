@@ -200,6 +200,15 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                          H > 1 ? o_sh : 0, (hipStream_t)stream));
 }
 
+int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
+                           int* workgroups) {
+  if (!waves_per_workgroup || !workgroups) return SAGE_ERR_NULL;
+  const int st = check_shape(B, N, H, D);
+  if (st != SAGE_OK) return st;
+  sage::attn_shape(B, N, H, D, waves_per_workgroup, workgroups);
+  return SAGE_OK;
+}
+
 const char* sage_status_string(int status) {
   switch (status) {
     case SAGE_OK: return "ok";

@@ -66,6 +66,9 @@ hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t
                           int H, int D, uint8_t* v_fp8, float* v_scale, float* v_mean,
                           void* workspace, hipStream_t stream);
 
+// Waves per workgroup and grid size of the attention launch for these sizes.
+void attn_shape(int B, int N, int H, int D, int* waves, int* workgroups);
+
 hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                            const float* v_mean, int B, int N, int H, int D, float sm_scale,

@@ -121,6 +121,21 @@ def test_workspace_sizes(sage):
     assert a % 256 == 0 and b % 256 == 0
 
 
+def test_attn_launch_shape(sage):
+    """Shallow grids (FLUX, B2 H24 N4608: 864 eight-wave workgroups, ~3.4 per
+    CU) take four-wave workgroups; deep ones (B1 H40 N32760: 20 per CU) eight."""
+    w, g = sage.sage_attn_launch_shape(2, 4608, 24, 128)
+    assert (w, g) == (4, 2 * 24 * 36)
+    w, g = sage.sage_attn_launch_shape(1, 32760, 40, 128)
+    assert w == 8 and g == 40 * 128
+    w, g = sage.sage_attn_launch_shape(1, 1, 1, 64)
+    assert g % 8 == 0 and g >= 1
+    with pytest.raises(sage.SageError) as e:
+        sage.sage_attn_launch_shape(1, 10, 2, 96)
+    assert e.value.status == -3
+    assert sage.lib().sage_attn_launch_shape(1, 10, 2, 64, None, None) == -1
+
+
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
     import quantized_attention_video_smooth_amd as s
     monkeypatch.setattr(s, "_lib", None)

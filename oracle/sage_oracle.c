@@ -231,17 +231,19 @@ void orc_quant_i8_blocks(const uint16_t* x, int64_t sb, int64_t sn, int64_t sh, 
 }
 
 /* Steps 1-4 as ONE routine (the fused form the report describes in card A:
- * center + BF16 round + quant with no K intermediate).  Q uses blocks of 32
- * tokens on raw Q (reading R5/R7: no smoothing and no softmax scale folded in),
- * K uses blocks of 64 tokens on the centred values (reading R4).
- * Outputs: q_i8/k_i8 [B][H][N][D], q_scale [B][H][ceil(N/32)],
+ * center + BF16 round + quant with no K intermediate).  Q uses blocks of
+ * q_block tokens on raw Q (reading R5/R7: no smoothing and no softmax scale
+ * folded in): 32 for the block granularity of the path, 1 for one scale per
+ * token (the finer "per-thread" granularity of §02 stage 03).  K uses blocks of
+ * 64 tokens on the centred values (reading R4).
+ * Outputs: q_i8/k_i8 [B][H][N][D], q_scale [B][H][ceil(N/q_block)],
  * k_scale [B][H][ceil(N/64)], k_mean [B][H][D] (bf16).
  * Returns the number of K channels whose fp64 sum is not provably exact. */
 int orc_quant_qk(const uint16_t* q, int64_t qsb, int64_t qsn, int64_t qsh,
                  const uint16_t* k, int64_t ksb, int64_t ksn, int64_t ksh,
-                 int B, int N, int H, int D,
+                 int B, int N, int H, int D, int q_block,
                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean) {
-  const int BQ = 32, BK = 64;
+  const int BQ = q_block, BK = 64;
   const int nq = (N + BQ - 1) / BQ, nk = (N + BK - 1) / BK;
   int bad = 0;
 #pragma omp parallel for collapse(2) reduction(+ : bad) schedule(dynamic)
@@ -278,7 +280,7 @@ int orc_quant_qk(const uint16_t* q, int64_t qsb, int64_t qsn, int64_t qsh,
             k_i8[(bh * N + j) * D + d] = (int8_t)((scale == 0.0f) ? 0 : orc_i8_code(c * inv));
           }
       }
-      /* Q INT8 per 32-token block (step 4) */
+      /* Q INT8 per q_block-token block (step 4) */
       for (int t = 0; t < nq; ++t) {
         const int j0 = t * BQ, j1 = (j0 + BQ < N) ? j0 + BQ : N;
         float a = 0.0f;
@@ -390,7 +392,7 @@ void orc_online_softmax_pv(const double* s, const double* vals, int n, int dv, i
 }
 
 /* Step 7: the quantised path in fp64 with the kernel's granularity.
- * For query i of head (b, h):  s_j = (sum_d q_i8[i,d] k_i8[j,d]) * q_scale[i/32]
+ * For query i of head (b, h):  s_j = (sum_d q_i8[i,d] k_i8[j,d]) * q_scale[i/q_block]
  * * sm_scale * k_scale[j/64]  (exact integer dot product, then fp64);
  * 64-key tiles, online softmax as above with FP8 P;
  * O[i,d] = (acc/l)[d] * v_scale[d] + v_mean[d]  (the V mean added back).
@@ -399,9 +401,9 @@ void orc_online_softmax_pv(const double* s, const double* vals, int n, int dv, i
  * out[B][H][nrows][D] in fp64. */
 void orc_attn_tiled(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                     const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
-                    int B, int N, int H, int D, double sm_scale, int bc,
+                    int B, int N, int H, int D, double sm_scale, int bc, int q_block,
                     const int32_t* rows, int nrows, double* out) {
-  const int nq = (N + 31) / 32, nk = (N + 63) / 64;
+  const int nq = (N + q_block - 1) / q_block, nk = (N + 63) / 64;
   const int64_t Np = ((int64_t)N + 63) / 64 * 64;
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h) {
@@ -418,7 +420,7 @@ void orc_attn_tiled(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8
         double* s = (double*)malloc(sizeof(double) * (size_t)N);
         double* o = out + (bh * nrows + r) * D;
         const int8_t* qi = q_i8 + (bh * N + i) * D;
-        const double cq = (double)q_scale[bh * nq + i / 32] * sm_scale;
+        const double cq = (double)q_scale[bh * nq + i / q_block] * sm_scale;
         for (int j = 0; j < N; ++j) {
           const int8_t* kj = k_i8 + (bh * N + j) * D;
           int64_t dot = 0;

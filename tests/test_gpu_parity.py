@@ -235,3 +235,41 @@ def test_quant_single_long_head(sage):
     assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
     _, _, _, qk, vq = _gpu_quant(sage, q, k, v)
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_degenerate_inputs(sage, D):
+    """Zero and subnormal quantisation blocks (scale 0, codes 0 through the
+    zero guard when 127/a or 448/a overflows), a head with constant K (all
+    scores 0: uniform attention) and a constant V channel (scale 0: the output
+    channel is bf16(v_mean) exactly)."""
+    cfg = synth.custom(2, 200, 3, D, tag=312)
+    _log(f"[parity] degenerate inputs B{cfg.B} N{cfg.N} H{cfg.H} D{D}")
+    q, k, v = synth.make_qkv(cfg)
+    tiny = torch.tensor(1e-40, dtype=torch.bfloat16)          # a bf16 subnormal
+    assert 0 < float(tiny) < 1.2e-38
+    q[:, 32:64] = 0                                           # a zero Q block, every head
+    q[:, 64:96, 0] = tiny                                     # a subnormal Q block of head 0
+    k[:, :, 2] = k[0, 0, 2]                                   # head 2: K constant over tokens
+    v[:, :, 1, 7] = 2.5                                       # a constant V channel
+    sign = torch.where(torch.arange(cfg.N) % 2 == 0, 1.0, -1.0).to(torch.bfloat16)
+    v[:, :, 0, 3] = tiny * sign[None, :]                      # a V channel of +-subnormals
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
+    assert np.all(ref_qk["q_scale"][:, :, 1] == 0) and np.all(ref_qk["q_scale"][:, 0, 2] == 0)
+    assert np.all(ref_qk["k_scale"][:, 2] == 0)
+    assert np.all(ref_v["v_scale"][:, 1, 7] == 0) and np.all(ref_v["v_scale"][:, 0, 3] == 0)
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+    torch.cuda.synchronize()
+    got = _rows_gathered(out, np.arange(cfg.N))
+    tiled = oracle.attn_tiled(ref_qk, ref_v)
+    assert oracle.rel_l2(got, tiled) <= TOL_ORACLE
+    # the constant channel comes back as bf16(v_mean) in every row
+    vm = torch.tensor(ref_v["v_mean"][:, 1, 7]).to(torch.bfloat16)
+    col = out[:, :, 1, 7].cpu()
+    assert torch.equal(col, vm[:, None].expand_as(col))
+    # head 2 (constant K): every query sees the same uniform weights
+    o2 = out[:, :, 2].float().cpu()
+    assert torch.equal(o2, o2[:, :1].expand_as(o2))

@@ -106,6 +106,37 @@ def test_int8_closed_forms(qkv):
     _check_int8_blocks(kc, out["k_i8"], out["k_scale"], 64)
 
 
+def test_per_token_q_closed_forms(qkv):
+    """One Q scale per token (the finer granularity of §02 stage 03): each
+    row is its own absmax block; K is untouched by the Q granularity."""
+    cfg, (q, k, v) = qkv
+    out1 = oracle.quant_qk(q, k, q_block=1)
+    out32 = oracle.quant_qk(q, k)
+    assert out1["q_scale"].shape == (cfg.B, cfg.H, cfg.N)
+    qf = q.float().numpy().transpose(0, 2, 1, 3)
+    _check_int8_blocks(qf, out1["q_i8"], out1["q_scale"], 1)
+    for key in ("k_i8", "k_scale", "k_mean"):
+        np.testing.assert_array_equal(out1[key], out32[key])
+    # a token's scale never exceeds its 32-token block's
+    blk = out32["q_scale"][:, :, np.arange(cfg.N) // 32]
+    assert np.all(out1["q_scale"] <= blk)
+
+
+def test_per_token_equals_block_when_rows_share_absmax():
+    """If every row of a 32-token block has the same absmax, per-token and
+    per-block quantisation are the same numbers, and so is the attention."""
+    B, N, H, D = 1, 100, 2, 64
+    rng = np.random.default_rng(9)
+    qv = rng.uniform(-1.0, 1.0, (B, N, H, D)).astype(np.float32)
+    qv[..., 5] = np.where(np.arange(N) % 2 == 0, 2.0, -2.0)[None, :, None]   # |x| = 2 is each row's max
+    q, k, v = _bf16(qv), _bf16(rng.standard_normal((B, N, H, D))), _bf16(rng.standard_normal((B, N, H, D)))
+    out1, out32 = oracle.quant_qk(q, k, q_block=1), oracle.quant_qk(q, k)
+    np.testing.assert_array_equal(out1["q_i8"], out32["q_i8"])
+    np.testing.assert_array_equal(out1["q_scale"], out32["q_scale"][:, :, np.arange(N) // 32])
+    vq = oracle.quant_v(v)
+    np.testing.assert_array_equal(oracle.attn_tiled(out1, vq), oracle.attn_tiled(out32, vq))
+
+
 def test_constant_k_channels_give_zero_codes():
     B, N, H, D = 1, 130, 2, 64
     rng = np.random.default_rng(5)

@@ -60,6 +60,12 @@ enum sage_status {
 #define SAGE_NPAD 64        /* token padding of the quantised layouts              */
 #define SAGE_PERM_VERSION 1 /* version of the V slot map below                     */
 
+/* Q scale granularity (q_block of the _ex entry points): one scale per 32-token
+ * block (SAGE_Q_BLOCK, what sage_quant_qk / sage_attn_fwd use) or one per token
+ * (SAGE_Q_TOKEN: the finer "per-thread" granularity of the report's §02 stage 03). */
+#define SAGE_Q_BLOCK 32
+#define SAGE_Q_TOKEN 1
+
 typedef struct {
   int32_t bq;             /* SAGE_BQ */
   int32_t bk;             /* SAGE_BK */
@@ -123,6 +129,20 @@ int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sage_quant_qk_ex -- sage_quant_qk with the Q scale granularity as an
+ * argument: q_block = SAGE_Q_BLOCK (32, identical to sage_quant_qk) or
+ * SAGE_Q_TOKEN (1): q_scale is then fp32 [B,H,Np], one scale per token,
+ *     q_scale = max_d |Q[t,d]| / 127,  q_i8 = clamp(rne(Q * (127 / max_d |Q[t,d]|)), -127, 127),
+ * with the same zero rule (entries for tokens N..Np-1 are 0).  K outputs do not
+ * depend on q_block.  Any other q_block returns SAGE_ERR_UNSUPPORTED.
+ */
+int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                     const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                     int B, int N, int H, int D,
+                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
+                     void* workspace, size_t workspace_bytes, int q_block, void* stream);
+
+/*
  * sage_quant_v -- V smoothing + FP8 E4M3 V, transposed, padded and permuted
  * (report card C "V alias + tiled transpose"; E4M3 per the A10 FLUX.1 page §1.1).
  *
@@ -170,6 +190,15 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale,
                   int B, int N, int H, int D, float sm_scale,
                   void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, void* stream);
 
+/* sage_attn_fwd on the outputs of sage_quant_qk_ex with the same q_block:
+ * query i uses q_scale[i / q_block].  q_block = SAGE_Q_BLOCK is sage_attn_fwd;
+ * any value other than SAGE_Q_BLOCK or SAGE_Q_TOKEN returns SAGE_ERR_UNSUPPORTED. */
+int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
+                     const int8_t* k_i8, const float* k_scale,
+                     const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
+                     int B, int N, int H, int D, float sm_scale,
+                     void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, void* stream);
+
 /* Launch shape that sage_attn_fwd uses for these sizes on the current device:
  * waves per workgroup (32 queries each) and workgroups launched.  Eight waves
  * (256 queries per workgroup, one per CU) when the grid is at least eight such
@@ -196,6 +225,19 @@ int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale,
                            const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
                            int B, int N, int H, int D,
                            const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh);
+/* The same checks for the _ex entry points (q_block last). */
+int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                              const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                              int B, int N, int H, int D,
+                              const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                              const float* k_scale, const uint16_t* k_mean,
+                              const void* workspace, size_t workspace_bytes, int q_block);
+int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
+                              const int8_t* k_i8, const float* k_scale,
+                              const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
+                              int B, int N, int H, int D,
+                              const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                              int q_block);
 
 /* Static, never-NULL description of a status code. */
 const char* sage_status_string(int status);

@@ -9,8 +9,9 @@
 //
 //   * a workgroup = 8 waves (256 queries) or 4 waves (128 queries, two
 //     workgroups per CU, chosen when the grid is shallow) of one (b, h); a
-//     wave owns 32 queries, which is exactly one Q quantisation block, so
-//     q_scale is a per-wave scalar;
+//     wave owns 32 queries, which is exactly one Q quantisation block (or,
+//     with one Q scale per token, lane l's query has its own scale: free in
+//     this layout, where each lane's scores belong to a single query);
 //   * the key loop walks 64-key tiles (one K quantisation block, so k_scale is
 //     a per-tile scalar) through an LDS ring filled with direct global->LDS
 //     loads (no VGPR staging) two or three tiles ahead, in an XOR-swizzled layout that
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_fp8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, int H, int N, int Np, int n_qtiles, int total_tiles,
-    float cq0, uint16_t* __restrict__ out, int64_t o_sb, int64_t o_sn, int64_t o_sh) {
+    int q_block, float cq0, uint16_t* __restrict__ out, int64_t o_sb, int64_t o_sn, int64_t o_sh) {
   using C = AttnCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NBUF * C::STAGE];
 
@@ -121,7 +122,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     const int8_t* qp = q_i8 + ((size_t)bh * Np + q0 + l32) * D + 16 * half;
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc) qop[dc] = *(const v4i*)(qp + 32 * dc);
-    cq = q_scale[(size_t)bh * (Np / 32) + q0 / 32] * cq0;
+    // the scale of this lane's query: one per 32-query block (the whole
+    // wave) or one per query (q_block == 1)
+    cq = q_scale[(size_t)bh * (Np / q_block) + (q0 + l32) / q_block] * cq0;
   } else {
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc) qop[dc] = v4i{0, 0, 0, 0};
@@ -355,8 +358,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 template <int D, int NW>
 hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                        const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                       const float* v_mean, int B, int N, int H, float sm_scale, uint16_t* out,
-                       int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
+                       const float* v_mean, int B, int N, int H, int q_block, float sm_scale,
+                       uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                       hipStream_t stream) {
   using C = AttnCfg<D, NW>;
   const int Np = (int)padded_tokens(N);
   const int n_qtiles = (int)ceil_div(N, C::QT);
@@ -364,8 +368,8 @@ hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k
   const int grid = (int)ceil_div(total, 8) * 8;
   const float cq0 = sm_scale * kLog2e;
   hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, q_i8, q_scale,
-                     k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, cq0, out, o_sb,
-                     o_sn, o_sh);
+                     k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, q_block, cq0,
+                     out, o_sb, o_sn, o_sh);
   return hipGetLastError();
 }
 
@@ -390,13 +394,13 @@ int attn_waves(int B, int N, int H) {
 template <int D>
 hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                     const float* v_mean, int B, int N, int H, float sm_scale, uint16_t* out,
-                     int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
+                     const float* v_mean, int B, int N, int H, int q_block, float sm_scale,
+                     uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
   if (attn_waves(B, N, H) == 8)
-    return attn_launch<D, 8>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, sm_scale,
-                             out, o_sb, o_sn, o_sh, stream);
-  return attn_launch<D, 4>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, sm_scale,
-                           out, o_sb, o_sn, o_sh, stream);
+    return attn_launch<D, 8>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
+                             sm_scale, out, o_sb, o_sn, o_sh, stream);
+  return attn_launch<D, 4>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
+                           sm_scale, out, o_sb, o_sn, o_sh, stream);
 }
 
 }  // namespace
@@ -410,14 +414,14 @@ void attn_shape(int B, int N, int H, int D, int* waves, int* workgroups) {
 
 hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                           const float* v_mean, int B, int N, int H, int D, float sm_scale,
-                           uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                           const float* v_mean, int B, int N, int H, int D, int q_block,
+                           float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
                            hipStream_t stream) {
   if (D == 128)
-    return attn_impl<128>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, sm_scale,
-                          out, o_sb, o_sn, o_sh, stream);
-  return attn_impl<64>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, sm_scale, out,
-                       o_sb, o_sn, o_sh, stream);
+    return attn_impl<128>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
+                          sm_scale, out, o_sb, o_sn, o_sh, stream);
+  return attn_impl<64>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
+                       sm_scale, out, o_sb, o_sn, o_sh, stream);
 }
 
 }  // namespace sage

@@ -93,15 +93,16 @@ size_t sage_quant_v_workspace_size(int B, int N, int H, int D) {
   return sage::v_workspace(B, N, H, D).bytes;
 }
 
-int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
-                           int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
-                           const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                           const float* k_scale, const uint16_t* k_mean, const void* workspace,
-                           size_t workspace_bytes) {
+int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                              const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
+                              int H, int D, const int8_t* q_i8, const float* q_scale,
+                              const int8_t* k_i8, const float* k_scale, const uint16_t* k_mean,
+                              const void* workspace, size_t workspace_bytes, int q_block) {
   if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !workspace)
     return SAGE_ERR_NULL;
   int st = check_shape(B, N, H, D);
   if (st != SAGE_OK) return st;
+  if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
   if ((st = check_strides(B, N, H, q_sb, q_sn, q_sh)) != SAGE_OK) return st;
   if ((st = check_strides(B, N, H, k_sb, k_sn, k_sh)) != SAGE_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
@@ -111,13 +112,23 @@ int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_
   const size_t need = sage::qk_workspace(B, N, H, D).bytes;
   if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
   const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
-  const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / 32) * 4),
+  const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / q_block) * 4),
                          range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / 64) * 4),
                          range_of(k_mean, bh * D * 2), range_of(workspace, need)};
   const Range ins[2] = {range_of(q, view_bytes(B, N, H, D, q_sb, q_sn, q_sh)),
                         range_of(k, view_bytes(B, N, H, D, k_sb, k_sn, k_sh))};
   if (any_overlap(outs, 6, ins, 2)) return SAGE_ERR_OVERLAP;
   return SAGE_OK;
+}
+
+int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+                           int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
+                           const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                           const float* k_scale, const uint16_t* k_mean, const void* workspace,
+                           size_t workspace_bytes) {
+  return sage_validate_quant_qk_ex(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8,
+                                   q_scale, k_i8, k_scale, k_mean, workspace, workspace_bytes,
+                                   SAGE_Q_BLOCK);
 }
 
 int sage_validate_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
@@ -140,14 +151,15 @@ int sage_validate_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_s
   return SAGE_OK;
 }
 
-int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                           const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                           const float* v_mean, int B, int N, int H, int D, const void* out,
-                           int64_t o_sb, int64_t o_sn, int64_t o_sh) {
+int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                              const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                              const float* v_mean, int B, int N, int H, int D, const void* out,
+                              int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !v_mean || !out)
     return SAGE_ERR_NULL;
   int st = check_shape(B, N, H, D);
   if (st != SAGE_OK) return st;
+  if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
   if ((st = check_strides(B, N, H, o_sb, o_sn, o_sh)) != SAGE_OK) return st;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_fp8) || !aligned16(out) ||
       ((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u) ||
@@ -155,7 +167,7 @@ int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_
     return SAGE_ERR_ALIGN;
   const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
   const Range outs[1] = {range_of(out, view_bytes(B, N, H, D, o_sb, o_sn, o_sh))};
-  const Range ins[7] = {range_of(q_i8, bh * Np * D),      range_of(q_scale, bh * (Np / 32) * 4),
+  const Range ins[7] = {range_of(q_i8, bh * Np * D),      range_of(q_scale, bh * (Np / q_block) * 4),
                         range_of(k_i8, bh * Np * D),      range_of(k_scale, bh * (Np / 64) * 4),
                         range_of(v_fp8, bh * D * Np),     range_of(v_scale, bh * D * 4),
                         range_of(v_mean, bh * D * 4)};
@@ -163,17 +175,34 @@ int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_
   return SAGE_OK;
 }
 
+int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                           const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                           const float* v_mean, int B, int N, int H, int D, const void* out,
+                           int64_t o_sb, int64_t o_sn, int64_t o_sh) {
+  return sage_validate_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, D,
+                                   out, o_sb, o_sn, o_sh, SAGE_Q_BLOCK);
+}
+
+int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+                     int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
+                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
+                     void* workspace, size_t workspace_bytes, int q_block, void* stream) {
+  const int st = sage_validate_quant_qk_ex(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D,
+                                           q_i8, q_scale, k_i8, k_scale, k_mean, workspace,
+                                           workspace_bytes, q_block);
+  if (st != SAGE_OK) return st;
+  return status_of(sage::launch_quant_qk((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
+                                         (const uint16_t*)k, B > 1 ? k_sb : 0, k_sn,
+                                         H > 1 ? k_sh : 0, B, N, H, D, q_block, q_i8, q_scale, k_i8,
+                                         k_scale, k_mean, workspace, (hipStream_t)stream));
+}
+
 int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
                   int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
                   int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
                   void* workspace, size_t workspace_bytes, void* stream) {
-  const int st = sage_validate_quant_qk(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8,
-                                        q_scale, k_i8, k_scale, k_mean, workspace, workspace_bytes);
-  if (st != SAGE_OK) return st;
-  return status_of(sage::launch_quant_qk((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
-                                         (const uint16_t*)k, B > 1 ? k_sb : 0, k_sn,
-                                         H > 1 ? k_sh : 0, B, N, H, D, q_i8, q_scale, k_i8, k_scale,
-                                         k_mean, workspace, (hipStream_t)stream));
+  return sage_quant_qk_ex(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8, q_scale, k_i8,
+                          k_scale, k_mean, workspace, workspace_bytes, SAGE_Q_BLOCK, stream);
 }
 
 int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N, int H, int D,
@@ -187,17 +216,25 @@ int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B,
                                         (hipStream_t)stream));
 }
 
+int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                     const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                     const float* v_mean, int B, int N, int H, int D, float sm_scale, void* out,
+                     int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, void* stream) {
+  const int st = sage_validate_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B,
+                                           N, H, D, out, o_sb, o_sn, o_sh, q_block);
+  if (st != SAGE_OK) return st;
+  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / __builtin_sqrtf((float)D);
+  return status_of(sage::launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N,
+                                         H, D, q_block, sm_scale, (uint16_t*)out, B > 1 ? o_sb : 0,
+                                         o_sn, H > 1 ? o_sh : 0, (hipStream_t)stream));
+}
+
 int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                   const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                   const float* v_mean, int B, int N, int H, int D, float sm_scale, void* out,
                   int64_t o_sb, int64_t o_sn, int64_t o_sh, void* stream) {
-  const int st = sage_validate_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N,
-                                        H, D, out, o_sb, o_sn, o_sh);
-  if (st != SAGE_OK) return st;
-  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / __builtin_sqrtf((float)D);
-  return status_of(sage::launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N,
-                                         H, D, sm_scale, (uint16_t*)out, B > 1 ? o_sb : 0, o_sn,
-                                         H > 1 ? o_sh : 0, (hipStream_t)stream));
+  return sage_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, D, sm_scale,
+                          out, o_sb, o_sn, o_sh, SAGE_Q_BLOCK, stream);
 }
 
 int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,

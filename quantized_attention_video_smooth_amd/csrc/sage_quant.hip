@@ -171,14 +171,15 @@ __global__ __launch_bounds__(D) void finalize_kernel(
 // ---------------------------------------------------------------------------
 // Fused K centre + BF16 round + INT8 (z = 0) and Q INT8 (z = 1).
 // grid (Np/64, B*H, 2), 256 threads; one 64-token x D tile per workgroup
-// (one K block, or two 32-token Q blocks).  Outputs are head-major [B,H,Np,D].
+// (one K block, or two 32-token Q blocks, or 64 per-token Q scales when
+// q_block == 1).  Outputs are head-major [B,H,Np,D].
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
     const uint16_t* __restrict__ q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
     const uint16_t* __restrict__ k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int H, int N, int Np,
     const uint16_t* __restrict__ k_mean, int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
-    int8_t* __restrict__ k_i8, float* __restrict__ k_scale) {
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int q_block) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
   constexpr int PASSES = 64 / RPP;
@@ -222,6 +223,32 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[p][j]));
     if (p < PASSES / 2) a_lo = fmaxf(a_lo, m); else a_hi = fmaxf(a_hi, m);
+  }
+  if (is_q && q_block == 1) {
+    // one scale per token: the row's absmax over the LPR consecutive lanes
+    // that hold it (a wave holds 64 / LPR whole rows)
+    int8_t* dst = q_i8 + ((size_t)bh * Np + t * 64) * D + lc * 8;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[p][j]));
+#pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+      const float iv = 127.0f / a;
+      const bool zero = (a == 0.0f) || !__builtin_isfinite(iv);
+      const float inv = zero ? 0.0f : iv;
+      const int rr = lr + p * RPP;
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w0 |= (uint32_t)(i8_code(x[p][j] * inv) & 0xFF) << (8 * j);
+        w1 |= (uint32_t)(i8_code(x[p][j + 4] * inv) & 0xFF) << (8 * j);
+      }
+      *(uint2*)(dst + (size_t)rr * D) = make_uint2(w0, w1);
+      if (lc == 0) q_scale[(size_t)bh * Np + t * 64 + rr] = zero ? 0.0f : a / 127.0f;
+    }
+    return;  // whole workgroup (is_q and q_block are uniform), before any barrier
   }
   a_lo = wave_max(a_lo);
   a_hi = wave_max(a_hi);
@@ -345,8 +372,8 @@ __global__ __launch_bounds__(kThreads) void v_quant_kernel(
 template <int D>
 hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                          const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
-                         int H, int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
-                         uint16_t* k_mean, void* ws, hipStream_t stream) {
+                         int H, int q_block, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                         float* k_scale, uint16_t* k_mean, void* ws, hipStream_t stream) {
   const StatsSplit s = stats_split(B, N, H);
   const QkWorkspace w = qk_workspace(B, N, H, D);
   char* wsb = (char*)ws;
@@ -363,7 +390,7 @@ hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t 
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((qk_quant_kernel<D>), dim3(Np / 64, B * H, 2), dim3(kThreads), 0, stream, q,
                      q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, H, N, Np, (const uint16_t*)k_mean, q_i8,
-                     q_scale, k_i8, k_scale);
+                     q_scale, k_i8, k_scale, q_block);
   return hipGetLastError();
 }
 
@@ -396,13 +423,13 @@ hipError_t quant_v_impl(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v
 
 hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                            const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
-                           int H, int D, int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                           int H, int D, int q_block, int8_t* q_i8, float* q_scale, int8_t* k_i8,
                            float* k_scale, uint16_t* k_mean, void* workspace, hipStream_t stream) {
   if (D == 128)
-    return quant_qk_impl<128>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_i8, q_scale, k_i8,
-                              k_scale, k_mean, workspace, stream);
-  return quant_qk_impl<64>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_i8, q_scale, k_i8,
-                           k_scale, k_mean, workspace, stream);
+    return quant_qk_impl<128>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, q_i8,
+                              q_scale, k_i8, k_scale, k_mean, workspace, stream);
+  return quant_qk_impl<64>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, q_i8, q_scale,
+                           k_i8, k_scale, k_mean, workspace, stream);
 }
 
 hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,

@@ -38,10 +38,10 @@ def sage():
     return s
 
 
-def _gpu_quant(sage, q, k, v):
+def _gpu_quant(sage, q, k, v, q_block=32):
     dev = torch.device("cuda")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    qk = sage.quant_qk(qd, kd)
+    qk = sage.quant_qk(qd, kd, q_block=q_block)
     vq = sage.quant_v(vd)
     torch.cuda.synchronize()
     return qd, kd, vd, qk, vq
@@ -50,7 +50,7 @@ def _gpu_quant(sage, q, k, v):
 def _check_quant_bits(qk, vq, ref_qk, ref_v, N):
     q_i8, q_scale, k_i8, k_scale, k_mean = [t.cpu() for t in qk]
     v_fp8, v_scale, v_mean = [t.cpu() for t in vq]
-    nq, nk = math.ceil(N / 32), math.ceil(N / 64)
+    nq, nk = math.ceil(N / ref_qk.get("q_block", 32)), math.ceil(N / 64)
     np.testing.assert_array_equal(q_i8[:, :, :N].numpy(), ref_qk["q_i8"])
     np.testing.assert_array_equal(k_i8[:, :, :N].numpy(), ref_qk["k_i8"])
     assert torch.all(q_i8[:, :, N:] == 0) and torch.all(k_i8[:, :, N:] == 0)
@@ -273,3 +273,90 @@ def test_degenerate_inputs(sage, D):
     # head 2 (constant K): every query sees the same uniform weights
     o2 = out[:, :, 2].float().cpu()
     assert torch.equal(o2, o2[:, :1].expand_as(o2))
+
+
+PER_TOKEN = [
+    synth.config(0),
+    synth.custom(2, 63, 3, 64, tag=302),
+    synth.custom(3, 200, 2, 128, tag=304),
+    synth.custom(1, 777, 4, 128, tag=305),
+]
+
+
+@pytest.mark.parametrize("cfg", PER_TOKEN, ids=lambda c: f"{c.name}-B{c.B}N{c.N}H{c.H}D{c.D}")
+def test_per_token_q_full(sage, cfg):
+    """One Q scale per token (q_block 1): codes and scales bit-exact against the
+    oracle's per-token quantiser, K and V outputs identical to the per-block
+    run, attention within the oracle bar."""
+    _log(f"[parity] per-token Q {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k, q_block=1), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v, q_block=1)
+    assert qk[1].shape[-1] == qk[0].shape[2]
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+    qk32 = sage.quant_qk(qd, kd)
+    torch.cuda.synchronize()
+    for a, b in zip(qk[2:], qk32[2:]):
+        assert torch.equal(a, b)
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+    torch.cuda.synchronize()
+    got = _rows_gathered(out, np.arange(cfg.N))
+    tiled = oracle.attn_tiled(ref_qk, ref_v)
+    exact = oracle.attn_exact(q, k, v)
+    e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
+    e_blk = oracle.rel_l2(oracle.attn_tiled(oracle.quant_qk(q, k), ref_v), exact)
+    _log(f"  rel L2: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}  "
+         f"per-block-oracle-vs-exact {e_blk:.3e}")
+    assert e_or <= TOL_ORACLE
+    assert e_ex <= max(TOL_EXACT, e_blk + TOL_ORACLE)
+
+
+def test_per_token_q_workload_sampled(sage):
+    """FLUX joint shape with per-token Q scales: quantised outputs bit-exact in
+    full, attention on every 16th query row."""
+    cfg = synth.config(1)
+    _log(f"[parity] per-token Q workload {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k, q_block=1), oracle.quant_v(v)
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v, q_block=1)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+    torch.cuda.synchronize()
+    rows = synth.query_subset(cfg.N, every=16)
+    got = _rows_gathered(out, rows)
+    tiled = oracle.attn_tiled(ref_qk, ref_v, rows=rows)
+    exact = oracle.attn_exact(q, k, v, rows=rows)
+    e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
+    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}")
+    assert e_or <= TOL_ORACLE and e_ex <= TOL_EXACT
+
+
+def test_plain_entry_points_equal_ex(sage):
+    """sage_quant_qk / sage_attn_fwd are the q_block 32 case of the _ex calls,
+    bit for bit."""
+    cfg = synth.custom(2, 300, 3, 128, tag=313)
+    q, k, v = (t.cuda() for t in synth.make_qkv(cfg))
+    B, N, H, D = q.shape
+    qk = sage.quant_qk(q, k)
+    vq = sage.quant_v(v)
+    out = sage.attn_fwd(*qk[:4], *vq, N=N)
+    torch.cuda.synchronize()
+    lib = sage.lib()
+    plain = [torch.empty_like(t) for t in qk]
+    ws = torch.empty(lib.sage_quant_qk_workspace_size(B, N, H, D), dtype=torch.uint8, device="cuda")
+    qs = [x for x in q.stride()[:3]]
+    ks = [x for x in k.stride()[:3]]
+    st = lib.sage_quant_qk(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D,
+                           *[t.data_ptr() for t in plain], ws.data_ptr(), ws.numel(),
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    o2 = torch.empty_like(out)
+    st = lib.sage_attn_fwd(*[t.data_ptr() for t in plain[:4]], *[t.data_ptr() for t in vq],
+                           B, N, H, D, 0.0, o2.data_ptr(), *o2.stride()[:3],
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    for a, b in zip(qk, plain):
+        assert torch.equal(a, b)
+    assert torch.equal(out, o2)

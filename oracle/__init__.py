@@ -61,11 +61,11 @@ def _load():
         "orc_k_center": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp], None),
         "orc_quant_i8_blocks": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp], None),
         "orc_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
-                          _i32, _vp, _vp, _vp, _vp, _vp], _i32),
+                          _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
         "orc_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
         "orc_online_softmax_pv": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp], None),
         "orc_attn_tiled": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _dbl, _i32,
-                            _i32, _vp, _i32, _vp], None),
+                            _i32, _i32, _vp, _i32, _vp], None),
         "orc_attn_exact": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                             _i32, _i32, _i32, _i32, _dbl, _vp, _i32, _vp], None),
         "orc_num_threads": ([], _i32),
@@ -129,13 +129,16 @@ def v_slot(t: int) -> int:
 
 # ---- quantisation ----------------------------------------------------------
 
-def quant_qk(q, k, q_block: int = BQ):
+def quant_qk(q, k, q_block: int = BQ, k_block: int = BK):
     """Fused steps 1-4.  Returns dict of numpy arrays:
-    q_i8 / k_i8 [B,H,N,D] int8, q_scale [B,H,ceil(N/q_block)], k_scale [B,H,ceil(N/64)] fp32,
-    k_mean [B,H,D] uint16 (bf16 bits), inexact (int: channels with a non-exact sum),
-    q_block.  q_block = 32 (the path's block granularity) or 1 (one scale per token)."""
+    q_i8 / k_i8 [B,H,N,D] int8, q_scale [B,H,ceil(N/q_block)], k_scale [B,H,ceil(N/k_block)]
+    fp32, k_mean [B,H,D] uint16 (bf16 bits), inexact (int: channels with a non-exact sum),
+    q_block, k_block.  q_block = 32 (the path's block granularity) or 1 (one scale per
+    token); k_block = 64 (the key tile) or 16."""
     if q_block not in (1, BQ):
         raise ValueError("q_block must be 32 or 1")
+    if k_block not in (16, BK):
+        raise ValueError("k_block must be 64 or 16")
     B, N, H, D = q.shape
     qb, qsb, qsn, qsh = _bf16_view(q)
     kb, ksb, ksn, ksh = _bf16_view(k)
@@ -143,14 +146,15 @@ def quant_qk(q, k, q_block: int = BQ):
         q_i8=np.empty((B, H, N, D), np.int8),
         q_scale=np.empty((B, H, math.ceil(N / q_block)), np.float32),
         k_i8=np.empty((B, H, N, D), np.int8),
-        k_scale=np.empty((B, H, math.ceil(N / BK)), np.float32),
+        k_scale=np.empty((B, H, math.ceil(N / k_block)), np.float32),
         k_mean=np.empty((B, H, D), np.uint16),
     )
     bad = _load().orc_quant_qk(_p(qb), qsb, qsn, qsh, _p(kb), ksb, ksn, ksh, B, N, H, D, q_block,
-                               _p(out["q_i8"]), _p(out["q_scale"]), _p(out["k_i8"]),
+                               k_block, _p(out["q_i8"]), _p(out["q_scale"]), _p(out["k_i8"]),
                                _p(out["k_scale"]), _p(out["k_mean"]))
     out["inexact"] = int(bad)
     out["q_block"] = q_block
+    out["k_block"] = k_block
     return out
 
 
@@ -230,7 +234,8 @@ def attn_tiled(qk: dict, v: dict, sm_scale: float | None = None, rows=None, bc: 
             np.ascontiguousarray(v["v_fp8"]), np.ascontiguousarray(v["v_scale"]),
             np.ascontiguousarray(v["v_mean"])]
     _load().orc_attn_tiled(*[_p(a) for a in arrs], B, N, H, D, float(sm_scale), bc,
-                           int(qk.get("q_block", BQ)), _p(rows), rows.size, _p(out))
+                           int(qk.get("q_block", BQ)), int(qk.get("k_block", BK)), _p(rows),
+                           rows.size, _p(out))
     return out
 
 

@@ -235,15 +235,16 @@ void orc_quant_i8_blocks(const uint16_t* x, int64_t sb, int64_t sn, int64_t sh, 
  * q_block tokens on raw Q (reading R5/R7: no smoothing and no softmax scale
  * folded in): 32 for the block granularity of the path, 1 for one scale per
  * token (the finer "per-thread" granularity of §02 stage 03).  K uses blocks of
- * 64 tokens on the centred values (reading R4).
+ * k_block tokens on the centred values: 64, the key tile (reading R4), or 16,
+ * a finer variant in the same direction.
  * Outputs: q_i8/k_i8 [B][H][N][D], q_scale [B][H][ceil(N/q_block)],
- * k_scale [B][H][ceil(N/64)], k_mean [B][H][D] (bf16).
+ * k_scale [B][H][ceil(N/k_block)], k_mean [B][H][D] (bf16).
  * Returns the number of K channels whose fp64 sum is not provably exact. */
 int orc_quant_qk(const uint16_t* q, int64_t qsb, int64_t qsn, int64_t qsh,
                  const uint16_t* k, int64_t ksb, int64_t ksn, int64_t ksh,
-                 int B, int N, int H, int D, int q_block,
+                 int B, int N, int H, int D, int q_block, int k_block,
                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean) {
-  const int BQ = q_block, BK = 64;
+  const int BQ = q_block, BK = k_block;
   const int nq = (N + BQ - 1) / BQ, nk = (N + BK - 1) / BK;
   int bad = 0;
 #pragma omp parallel for collapse(2) reduction(+ : bad) schedule(dynamic)
@@ -260,7 +261,7 @@ int orc_quant_qk(const uint16_t* q, int64_t qsb, int64_t qsn, int64_t qsh,
         k_mean[bh * D + d] = m16;
         mean[d] = orc_bf16_value(m16);
       }
-      /* K center + round + INT8 per 64-token block (steps 2-3) */
+      /* K center + round + INT8 per k_block-token block (steps 2-3) */
       for (int t = 0; t < nk; ++t) {
         const int j0 = t * BK, j1 = (j0 + BK < N) ? j0 + BK : N;
         float a = 0.0f;
@@ -393,7 +394,7 @@ void orc_online_softmax_pv(const double* s, const double* vals, int n, int dv, i
 
 /* Step 7: the quantised path in fp64 with the kernel's granularity.
  * For query i of head (b, h):  s_j = (sum_d q_i8[i,d] k_i8[j,d]) * q_scale[i/q_block]
- * * sm_scale * k_scale[j/64]  (exact integer dot product, then fp64);
+ * * sm_scale * k_scale[j/k_block]  (exact integer dot product, then fp64);
  * 64-key tiles, online softmax as above with FP8 P;
  * O[i,d] = (acc/l)[d] * v_scale[d] + v_mean[d]  (the V mean added back).
  * Inputs in the layouts produced by orc_quant_qk / orc_quant_v.
@@ -401,9 +402,9 @@ void orc_online_softmax_pv(const double* s, const double* vals, int n, int dv, i
  * out[B][H][nrows][D] in fp64. */
 void orc_attn_tiled(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                     const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
-                    int B, int N, int H, int D, double sm_scale, int bc, int q_block,
+                    int B, int N, int H, int D, double sm_scale, int bc, int q_block, int k_block,
                     const int32_t* rows, int nrows, double* out) {
-  const int nq = (N + q_block - 1) / q_block, nk = (N + 63) / 64;
+  const int nq = (N + q_block - 1) / q_block, nk = (N + k_block - 1) / k_block;
   const int64_t Np = ((int64_t)N + 63) / 64 * 64;
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h) {
@@ -425,7 +426,7 @@ void orc_attn_tiled(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8
           const int8_t* kj = k_i8 + (bh * N + j) * D;
           int64_t dot = 0;
           for (int d = 0; d < D; ++d) dot += (int64_t)qi[d] * (int64_t)kj[d];
-          s[j] = (double)dot * cq * (double)k_scale[bh * nk + j / 64];
+          s[j] = (double)dot * cq * (double)k_scale[bh * nk + j / k_block];
         }
         orc_online_softmax_pv(s, vals, N, D, bc, 1, o);
         for (int d = 0; d < D; ++d) o[d] = o[d] * (double)v_scale[bh * D + d] + (double)v_mean[bh * D + d];

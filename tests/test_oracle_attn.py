@@ -109,13 +109,13 @@ def test_exact_rows_sum_to_one(case):
     np.testing.assert_allclose(oracle.attn_exact(q, k, ones), 1.0, rtol=0, atol=1e-14)
 
 
-@pytest.mark.parametrize("q_block", [32, 1])
-def test_tiled_wiring_matches_numpy(case, q_block):
+@pytest.mark.parametrize("q_block,k_block", [(32, 64), (1, 64), (32, 16), (1, 16)])
+def test_tiled_wiring_matches_numpy(case, q_block, k_block):
     """Step 7 indexing: scores from INT8 codes with the per-32 (or per-token) Q
-    and per-64 K scales, V codes read back through the slot map, V scale and
-    mean applied."""
+    and per-64 (or per-16) K scales, V codes read back through the slot map,
+    V scale and mean applied."""
     cfg, q, k, v = case
-    qk, vq = oracle.quant_qk(q, k, q_block=q_block), oracle.quant_v(v)
+    qk, vq = oracle.quant_qk(q, k, q_block=q_block, k_block=k_block), oracle.quant_v(v)
     B, N, H, D = q.shape
     rows = np.array(sorted({0, 1, 31, 32, N // 2, N - 1}), np.int32)
     got = oracle.attn_tiled(qk, vq, rows=rows)
@@ -128,7 +128,7 @@ def test_tiled_wiring_matches_numpy(case, q_block):
             vals = oracle.e4m3_decode(vq["v_fp8"][b, h][:, cols]).T          # [N, D]
             for r, i in enumerate(rows):
                 dots = kd @ qk["q_i8"][b, h, i].astype(np.int64)
-                s = dots * (float(qk["q_scale"][b, h, i // q_block]) * sm) * qk["k_scale"][b, h, np.arange(N) // 64].astype(np.float64)
+                s = dots * (float(qk["q_scale"][b, h, i // q_block]) * sm) * qk["k_scale"][b, h, np.arange(N) // k_block].astype(np.float64)
                 o = oracle.online_softmax_pv(s, vals, 64, True)
                 want = o * vq["v_scale"][b, h] + vq["v_mean"][b, h]
                 np.testing.assert_allclose(got[b, h, r], want, rtol=1e-12, atol=1e-12)

@@ -137,6 +137,47 @@ def test_per_token_equals_block_when_rows_share_absmax():
     np.testing.assert_array_equal(oracle.attn_tiled(out1, vq), oracle.attn_tiled(out32, vq))
 
 
+def test_k16_closed_forms(qkv):
+    """16-token K blocks: closed-form quantiser properties per 16-token block of
+    the centred K; Q and the K mean do not depend on the K granularity; the
+    largest of the four 16-token scales inside a 64-token block is that
+    block's scale exactly (a/127 is monotone in a)."""
+    cfg, (q, k, v) = qkv
+    out16 = oracle.quant_qk(q, k, k_block=16)
+    out64 = oracle.quant_qk(q, k)
+    assert out16["k_scale"].shape == (cfg.B, cfg.H, math.ceil(cfg.N / 16))
+    mean, _ = oracle.k_mean(k)
+    kc = _f(oracle.k_center(k, mean)).transpose(0, 2, 1, 3)
+    _check_int8_blocks(kc, out16["k_i8"], out16["k_scale"], 16)
+    for key in ("q_i8", "q_scale", "k_mean"):
+        np.testing.assert_array_equal(out16[key], out64[key])
+    n16 = out16["k_scale"].shape[-1]
+    for t in range(out64["k_scale"].shape[-1]):
+        sub = out16["k_scale"][:, :, 4 * t:min(4 * t + 4, n16)]
+        np.testing.assert_array_equal(sub.max(-1), out64["k_scale"][:, :, t])
+
+
+def test_k16_equals_k64_when_subblocks_share_absmax():
+    """K built from +-x token pairs has a channel mean of exactly 0, so the
+    centred K is K itself; with |x| = 2 planted in every token, each 16-token
+    block has the 64-token block's absmax, and both granularities give the
+    same codes, the same (repeated) scales and the same attention."""
+    B, N, H, D = 1, 100, 2, 64
+    rng = np.random.default_rng(11)
+    half = rng.uniform(-1.0, 1.0, (B, N // 2, H, D)).astype(np.float32)
+    half[..., 5] = 2.0
+    kv = np.empty((B, N, H, D), np.float32)
+    kv[:, 0::2], kv[:, 1::2] = half, -half
+    k = _bf16(kv)
+    q, v = _bf16(rng.standard_normal((B, N, H, D))), _bf16(rng.standard_normal((B, N, H, D)))
+    out16, out64 = oracle.quant_qk(q, k, k_block=16), oracle.quant_qk(q, k)
+    assert np.all(out64["k_mean"] == 0)
+    np.testing.assert_array_equal(out16["k_i8"], out64["k_i8"])
+    np.testing.assert_array_equal(out16["k_scale"], out64["k_scale"][:, :, np.arange(7) // 4])
+    vq = oracle.quant_v(v)
+    np.testing.assert_array_equal(oracle.attn_tiled(out16, vq), oracle.attn_tiled(out64, vq))
+
+
 def test_constant_k_channels_give_zero_codes():
     B, N, H, D = 1, 130, 2, 64
     rng = np.random.default_rng(5)

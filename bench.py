@@ -28,11 +28,11 @@ PEAK_MFMA_TFLOPS = 5000.0   # MI355X dense INT8 / FP8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def algorithmic(B, N, H, D, q_block=32):
+def algorithmic(B, N, H, D, q_block=32, k_block=64):
     """Algorithmic work of each kernel (what the method must do; no padding,
     no second read of a two-pass design)."""
     E = B * N * H * D
-    nq, nk = math.ceil(N / q_block), math.ceil(N / 64)
+    nq, nk = math.ceil(N / q_block), math.ceil(N / k_block)
     return {
         "attn_ops": 4.0 * B * H * N * N * D,
         # Q: 2 B read + 1 B write per element + 4 B per scale (per 32-token block or token)
@@ -48,16 +48,16 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_src, workload, q_block):
+def traffic_record(kernel_src, workload, q_block, k_block):
     """HBM traffic per launch from the committed counter summary of this
-    workload, if it was taken on the current kernel source with the same Q
-    scale granularity (else None)."""
+    workload, if it was taken on the current kernel source with the same
+    scale granularities (else None)."""
     p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_counters.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
     if rec.get("source_sha256_16") != source_hash(kernel_src) or rec.get("workload") != workload \
-            or rec.get("q_block", 32) != q_block:
+            or rec.get("q_block", 32) != q_block or rec.get("k_block", 64) != k_block:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -108,6 +108,8 @@ def main():
                          "independent); attention waits for both. 1: all three calls in order")
     ap.add_argument("--q-block", type=int, choices=[32, 1], default=32,
                     help="Q scale granularity: one scale per 32-token block (default) or per token")
+    ap.add_argument("--k-block", type=int, choices=[64, 16], default=64,
+                    help="K scale granularity: one scale per 64-token key tile (default) or per 16 tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the run, copy 256 MiB device to device once: a kernel of known "
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counter readings")
@@ -136,7 +138,8 @@ def main():
     qb = args.q_block
     q_scale = torch.empty((B, H, Np // qb), dtype=torch.float32, device=dev)
     k_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
-    k_scale = torch.empty((B, H, Np // 64), dtype=torch.float32, device=dev)
+    kbl = args.k_block
+    k_scale = torch.empty((B, H, Np // kbl), dtype=torch.float32, device=dev)
     k_mean = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     v_fp8 = torch.empty((B, H, D, Np), dtype=torch.uint8, device=dev)
     v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
@@ -161,13 +164,13 @@ def main():
                               v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), side_p)
         st |= lib.sage_quant_qk_ex(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, q_i8.data_ptr(),
                                 q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
-                                k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, sp)
+                                k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp)
         ev_in[1].record(side)
         stream.wait_event(ev_in[1])
         if do_attn:
             st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
                                     k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
-                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, sp)
+                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, kbl, sp)
         if st != 0:
             raise RuntimeError(f"libsage call failed with status {st}")
 
@@ -179,7 +182,7 @@ def main():
             evs[0].record(stream)
         st = lib.sage_quant_qk_ex(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, q_i8.data_ptr(),
                                q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
-                               k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, sp)
+                               k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp)
         if evs:
             evs[1].record(stream)
         st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
@@ -189,7 +192,7 @@ def main():
         if do_attn:
             st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
                                     k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
-                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, sp)
+                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, kbl, sp)
         if evs:
             evs[3].record(stream)
         if st != 0:
@@ -224,14 +227,14 @@ def main():
     mn = {k2: min(v2) for k2, v2 in per.items()}
     p90 = {k2: sorted(v2)[min(len(v2) - 1, (9 * len(v2)) // 10)] for k2, v2 in per.items()}
 
-    work = algorithmic(B, N, H, D, qb)
+    work = algorithmic(B, N, H, D, qb, kbl)
     waves, wgs = sage.sage_attn_launch_shape(B, N, H, D)
     step_s = ms_per_step * 1e-3
     if do_attn:
         value = work["attn_ops"] / step_s / 1e12
         attn_tflops = work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12
         roofline = {
-            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}>: {waves}-wave workgroups, "
+            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave workgroups, "
                       f"{wgs} per launch)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
@@ -239,7 +242,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": traffic_record(os.path.join(ROOT, "quantized_attention_video_smooth_amd",
-                                                   "csrc", "sage_attn.hip"), cfg.name, qb),
+                                                   "csrc", "sage_attn.hip"), cfg.name, qb, kbl),
         }
         unit = "TFLOPS"
     else:
@@ -266,7 +269,7 @@ def main():
         "data": "synthetic (seeded counter-based normals, bf16 NHD)",
         "config": {"workload": cfg.name, "B": B, "N": N, "H": H, "D": D, "causal": False,
                    "layout": "NHD bf16 in, bf16 out", "seed": args.seed,
-                   "streams": args.streams, "q_block": qb},
+                   "streams": args.streams, "q_block": qb, "k_block": kbl},
         "kernels_ms": {k2: {"avg": round(avg[k2], 5), "median": round(med[k2], 5),
                             "min": round(mn[k2], 5), "p90": round(p90[k2], 5)} for k2 in per},
         "attn_tflops": round(work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12, 2) if do_attn else None,

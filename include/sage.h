@@ -65,6 +65,11 @@ enum sage_status {
  * (SAGE_Q_TOKEN: the finer "per-thread" granularity of the report's §02 stage 03). */
 #define SAGE_Q_BLOCK 32
 #define SAGE_Q_TOKEN 1
+/* K scale granularity (k_block of the _ex entry points): one scale per 64-token
+ * block, the attention key tile (SAGE_K_BLOCK, what sage_quant_qk / sage_attn_fwd
+ * use), or per 16-token block (SAGE_K_FINE: four scales per key tile). */
+#define SAGE_K_BLOCK 64
+#define SAGE_K_FINE 16
 
 typedef struct {
   int32_t bq;             /* SAGE_BQ */
@@ -129,18 +134,24 @@ int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * sage_quant_qk_ex -- sage_quant_qk with the Q scale granularity as an
- * argument: q_block = SAGE_Q_BLOCK (32, identical to sage_quant_qk) or
- * SAGE_Q_TOKEN (1): q_scale is then fp32 [B,H,Np], one scale per token,
- *     q_scale = max_d |Q[t,d]| / 127,  q_i8 = clamp(rne(Q * (127 / max_d |Q[t,d]|)), -127, 127),
- * with the same zero rule (entries for tokens N..Np-1 are 0).  K outputs do not
- * depend on q_block.  Any other q_block returns SAGE_ERR_UNSUPPORTED.
+ * sage_quant_qk_ex -- sage_quant_qk with the scale granularities as arguments
+ * (finer steps toward the per-thread scales of the report's §02 stage 03).
+ * q_block = SAGE_Q_BLOCK (32) or SAGE_Q_TOKEN (1): q_scale is fp32
+ * [B,H,Np/q_block]; with 1, one scale per token,
+ *     q_scale = max_d |Q[t,d]| / 127,  q_i8 = clamp(rne(Q * (127 / max_d |Q[t,d]|)), -127, 127).
+ * k_block = SAGE_K_BLOCK (64) or SAGE_K_FINE (16): k_scale is fp32
+ * [B,H,Np/k_block], the same absmax rule over k_block centred tokens.
+ * The zero rule is unchanged (entries for blocks wholly beyond N are 0); the
+ * Q outputs do not depend on k_block nor the K outputs on q_block, and
+ * (SAGE_Q_BLOCK, SAGE_K_BLOCK) is sage_quant_qk bit for bit.  Other values
+ * return SAGE_ERR_UNSUPPORTED.
  */
 int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                      const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
                      int B, int N, int H, int D,
                      int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
-                     void* workspace, size_t workspace_bytes, int q_block, void* stream);
+                     void* workspace, size_t workspace_bytes, int q_block, int k_block,
+                     void* stream);
 
 /*
  * sage_quant_v -- V smoothing + FP8 E4M3 V, transposed, padded and permuted
@@ -190,14 +201,17 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale,
                   int B, int N, int H, int D, float sm_scale,
                   void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, void* stream);
 
-/* sage_attn_fwd on the outputs of sage_quant_qk_ex with the same q_block:
- * query i uses q_scale[i / q_block].  q_block = SAGE_Q_BLOCK is sage_attn_fwd;
- * any value other than SAGE_Q_BLOCK or SAGE_Q_TOKEN returns SAGE_ERR_UNSUPPORTED. */
+/* sage_attn_fwd on the outputs of sage_quant_qk_ex with the same q_block and
+ * k_block: s_j uses q_scale[i / q_block] * k_scale[j / k_block].  The running
+ * max is still taken per 64-key tile.  (SAGE_Q_BLOCK, SAGE_K_BLOCK) is
+ * sage_attn_fwd; values other than those of sage_quant_qk_ex return
+ * SAGE_ERR_UNSUPPORTED. */
 int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
                      const int8_t* k_i8, const float* k_scale,
                      const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
                      int B, int N, int H, int D, float sm_scale,
-                     void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, void* stream);
+                     void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block,
+                     void* stream);
 
 /* Launch shape that sage_attn_fwd uses for these sizes on the current device:
  * waves per workgroup (32 queries each) and workgroups launched.  Eight waves
@@ -225,19 +239,20 @@ int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale,
                            const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
                            int B, int N, int H, int D,
                            const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh);
-/* The same checks for the _ex entry points (q_block last). */
+/* The same checks for the _ex entry points (q_block and k_block last). */
 int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                               const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
                               int B, int N, int H, int D,
                               const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint16_t* k_mean,
-                              const void* workspace, size_t workspace_bytes, int q_block);
+                              const void* workspace, size_t workspace_bytes, int q_block,
+                              int k_block);
 int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
                               const int8_t* k_i8, const float* k_scale,
                               const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
                               int B, int N, int H, int D,
                               const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
-                              int q_block);
+                              int q_block, int k_block);
 
 /* Static, never-NULL description of a status code. */
 const char* sage_status_string(int status);

@@ -53,13 +53,13 @@ _SIGS = {
                                 _vp, _i64, _i64, _i64], _i32),
     "sage_attn_launch_shape": ([_i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "sage_quant_qk_ex": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
-                          _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _vp], _i32),
+                          _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _vp], _i32),
     "sage_attn_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
-                          _vp, _i64, _i64, _i64, _i32, _vp], _i32),
+                          _vp, _i64, _i64, _i64, _i32, _i32, _vp], _i32),
     "sage_validate_quant_qk_ex": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
-                                   _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i32], _i32),
+                                   _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32], _i32),
     "sage_validate_attn_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                   _vp, _i64, _i64, _i64, _i32], _i32),
+                                   _vp, _i64, _i64, _i64, _i32, _i32], _i32),
     "sage_status_string": ([_i32], ctypes.c_char_p),
 }
 
@@ -168,10 +168,10 @@ def _nhd(t, name):
     return t.stride(0), t.stride(1), t.stride(2)
 
 
-def quant_qk(q, k, stream=None, q_block: int = 32):
+def quant_qk(q, k, stream=None, q_block: int = 32, k_block: int = 64):
     """K smoothing + INT8 K and INT8 Q.  Returns (q_i8 [B,H,Np,D], q_scale [B,H,Np/q_block],
-    k_i8 [B,H,Np,D], k_scale [B,H,Np/64], k_mean [B,H,D] bf16).  q_block: 32 (one Q scale
-    per 32-token block) or 1 (one per token)."""
+    k_i8 [B,H,Np,D], k_scale [B,H,Np/k_block], k_mean [B,H,D] bf16).  q_block: 32 (one Q
+    scale per 32-token block) or 1 (one per token); k_block: 64 or 16 tokens per K scale."""
     import torch
     B, N, H, D = q.shape
     if tuple(k.shape) != (B, N, H, D):
@@ -182,15 +182,17 @@ def quant_qk(q, k, stream=None, q_block: int = 32):
     q_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
     if q_block not in (1, BQ):
         raise ValueError("q_block must be 32 or 1")
+    if k_block not in (16, 64):
+        raise ValueError("k_block must be 64 or 16")
     q_scale = torch.empty((B, H, Np // q_block), dtype=torch.float32, device=dev)
     k_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
-    k_scale = torch.empty((B, H, Np // BK), dtype=torch.float32, device=dev)
+    k_scale = torch.empty((B, H, Np // k_block), dtype=torch.float32, device=dev)
     k_mean = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     need = sage_quant_qk_workspace_size(B, N, H, D)
     ws = workspace(dev, need)
     _check(sage_quant_qk_ex(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D,
                             q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
-                            k_mean.data_ptr(), ws.data_ptr(), ws.numel(), q_block,
+                            k_mean.data_ptr(), ws.data_ptr(), ws.numel(), q_block, k_block,
                             _stream_ptr(stream)),
            "sage_quant_qk_ex")
     return q_i8, q_scale, k_i8, k_scale, k_mean
@@ -232,16 +234,18 @@ def workspace_v(device, nbytes: int):
 def attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, N: int, sm_scale: float | None = None,
              out=None, stream=None):
     """Fused attention on the quantised operands; returns bf16 [B,N,H,D] (or fills `out`).
-    The Q scale granularity follows q_scale's length (Np/32 per head, or Np)."""
+    The scale granularities follow the scale lengths: q_scale Np/32 or Np per head,
+    k_scale Np/64 or Np/16."""
     import torch
     B, H, Np, D = q_i8.shape
     q_block = Np // q_scale.shape[-1]
+    k_block = Np // k_scale.shape[-1]
     if out is None:
         out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q_i8.device)
     os_ = _nhd(out, "out")
     _check(sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
                             v_fp8.data_ptr(), v_scale.data_ptr(), v_mean.data_ptr(), B, N, H, D,
-                            float(sm_scale) if sm_scale else 0.0, out.data_ptr(), *os_, q_block,
+                            float(sm_scale) if sm_scale else 0.0, out.data_ptr(), *os_, q_block, k_block,
                             _stream_ptr(stream)),
            "sage_attn_fwd_ex")
     return out

@@ -13,7 +13,9 @@
 //     with one Q scale per token, lane l's query has its own scale: free in
 //     this layout, where each lane's scores belong to a single query);
 //   * the key loop walks 64-key tiles (one K quantisation block, so k_scale is
-//     a per-tile scalar) through an LDS ring filled with direct global->LDS
+//     a per-tile scalar; with 16-token K blocks, each 16-key block of a tile
+//     lands in a fixed set of 8 accumulator registers per lane, so each set
+//     gets its own scalar) through an LDS ring filled with direct global->LDS
 //     loads (no VGPR staging) two or three tiles ahead, in an XOR-swizzled layout that
 //     keeps the MFMA operand reads free of bank conflicts;
 //   * S^T = K Q^T with v_mfma_i32_32x32x32_i8 (exact int32).  In that layout
@@ -84,12 +86,17 @@ __device__ __forceinline__ int xhalf_max(int v) {
   auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return max((int)r[0], (int)r[1]);
 }
+__device__ __forceinline__ float xhalf_maxf(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
 __device__ __forceinline__ float xhalf_sum(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-template <int D, int NW>
+// KB: K quantisation block (64: one scale per key tile; 16: four per tile).
+template <int D, int NW, int KB>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
@@ -132,7 +139,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 
   const int8_t* kbase = k_i8 + (size_t)bh * Np * D;
   const uint8_t* vbase = v_fp8 + (size_t)bh * D * Np;
-  const float* ksc = k_scale + (size_t)bh * ntiles;
+  static_assert(KB == 64 || KB == 16, "K block is 64 or 16 tokens");
+  constexpr int KPT = 64 / KB;  // K scales per key tile
+  const float* ksc = k_scale + (size_t)bh * ntiles * KPT;
 
   // ---- global -> LDS staging: direct loads (global_load_lds_dwordx4) ----
   // Instruction i of wave w fills tile chunk positions g = (i*NW + w)*64 + lane
@@ -176,7 +185,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
   v8i pop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  float ksc_cur = ksc[0];  // k_scale of the tile whose softmax is next
+  float ksc_cur[KPT];  // k_scale(s) of the tile whose softmax is next
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) ksc_cur[j] = ksc[j];
 
   // S^T(t) = K(t) Q^T into sdst (operands read from LDS slot t % 3).
   auto qk_mfma = [&](int t, v16i (&sdst)[2]) __attribute__((always_inline)) {
@@ -211,8 +222,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   // E4M3 (byte 16*kb + i of pop), row sum, accumulator rescale.
   auto softmax = [&](int t, v16i (&scur)[2], auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const float c = cq * ksc_cur;
-    const float ksc_next = ksc[min(t + 1, ntiles - 1)];  // used by the next tile
+    // c[j]: score multiplier of K block j of the tile; with KB = 16, block j
+    // holds keys 16j..16j+15 = registers 8*(j%2)..+8 of scur[j/2]
+    float c[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) c[j] = cq * ksc_cur[j];
+    float ksc_next[KPT];  // used by the next tile
+    const int tn = min(t + 1, ntiles - 1);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) ksc_next[j] = ksc[tn * KPT + j];
     // key index of scur[kb][i] inside the tile: 32*kb + 8*(i/4) + 4*half + i%4
     const int nvalid = N - t * 64;  // keys at or beyond nvalid are padding
     if constexpr (MASKED) {
@@ -224,13 +242,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
           if (key >= nvalid) scur[kb][i] = INT32_MIN;
         }
     }
-    int mxi = scur[0][0];
+    float m_tile;
+    if constexpr (KPT == 1) {
+      int mxi = scur[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mxi = max(mxi, scur[kb][i]);
-    mxi = xhalf_max(mxi);
-    const float m_new = fmaxf(m_run, (float)mxi * c);
+        for (int i = 0; i < 16; ++i) mxi = max(mxi, scur[kb][i]);
+      m_tile = (float)xhalf_max(mxi) * c[0];
+    } else {
+      // integer max per 16-key block, then scaled (every multiplier >= 0);
+      // a block wholly beyond N (scale 0) must not contribute its 0
+      m_tile = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int mb = scur[j >> 1][8 * (j & 1)];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mb = max(mb, scur[j >> 1][8 * (j & 1) + i]);
+        float v = (float)mb * c[j];
+        if constexpr (MASKED) {
+          if (16 * j >= nvalid) v = -__builtin_inff();
+        }
+        m_tile = fmaxf(m_tile, v);
+      }
+      m_tile = xhalf_maxf(m_tile);
+    }
+    const float m_new = fmaxf(m_run, m_tile);
     const float bias = kLog2_448 - m_new;
     float lsum = 0.0f;
 #pragma unroll
@@ -241,7 +278,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf((float)scur[kb][i], c, bias));
+          float x = __builtin_amdgcn_exp2f(
+              __builtin_fmaf((float)scur[kb][i], c[KPT == 1 ? 0 : 2 * kb + (r >> 1)], bias));
           if constexpr (MASKED) {
             const int key = 32 * kb + 8 * r + 4 * half + e;
             if (key >= nvalid) x = 0.0f;
@@ -272,7 +310,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     }
     l_run += lsum;
     m_run = m_new;
-    ksc_cur = ksc_next;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) ksc_cur[j] = ksc_next[j];
   };
 
   // One tile: start the direct loads of tile t+AHEAD into the ring slot of
@@ -355,7 +394,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int KB>
 hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                        const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                        const float* v_mean, int B, int N, int H, int q_block, float sm_scale,
@@ -367,7 +406,7 @@ hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k
   const int total = B * H * n_qtiles;
   const int grid = (int)ceil_div(total, 8) * 8;
   const float cq0 = sm_scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, q_i8, q_scale,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, KB>), dim3(grid), dim3(C::NT), 0, stream, q_i8, q_scale,
                      k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, q_block, cq0,
                      out, o_sb, o_sn, o_sh);
   return hipGetLastError();
@@ -391,16 +430,16 @@ int attn_waves(int B, int N, int H) {
   return wg8 >= 8 * (int64_t)ncu ? 8 : 4;
 }
 
-template <int D>
+template <int D, int KB>
 hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                      const float* v_mean, int B, int N, int H, int q_block, float sm_scale,
                      uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
   if (attn_waves(B, N, H) == 8)
-    return attn_launch<D, 8>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
-                             sm_scale, out, o_sb, o_sn, o_sh, stream);
-  return attn_launch<D, 4>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
-                           sm_scale, out, o_sb, o_sn, o_sh, stream);
+    return attn_launch<D, 8, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H,
+                                 q_block, sm_scale, out, o_sb, o_sn, o_sh, stream);
+  return attn_launch<D, 4, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H,
+                               q_block, sm_scale, out, o_sb, o_sn, o_sh, stream);
 }
 
 }  // namespace
@@ -415,13 +454,14 @@ void attn_shape(int B, int N, int H, int D, int* waves, int* workgroups) {
 hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                            const float* v_mean, int B, int N, int H, int D, int q_block,
-                           float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
-                           hipStream_t stream) {
-  if (D == 128)
-    return attn_impl<128>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
-                          sm_scale, out, o_sb, o_sn, o_sh, stream);
-  return attn_impl<64>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,
-                       sm_scale, out, o_sb, o_sn, o_sh, stream);
+                           int k_block, float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn,
+                           int64_t o_sh, hipStream_t stream) {
+#define SAGE_ATTN_IMPL(DD, KK)                                                                    \
+  attn_impl<DD, KK>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,      \
+                    sm_scale, out, o_sb, o_sn, o_sh, stream)
+  if (D == 128) return k_block == 16 ? SAGE_ATTN_IMPL(128, 16) : SAGE_ATTN_IMPL(128, 64);
+  return k_block == 16 ? SAGE_ATTN_IMPL(64, 16) : SAGE_ATTN_IMPL(64, 64);
+#undef SAGE_ATTN_IMPL
 }
 
 }  // namespace sage

@@ -97,12 +97,14 @@ int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t
                               const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
                               int H, int D, const int8_t* q_i8, const float* q_scale,
                               const int8_t* k_i8, const float* k_scale, const uint16_t* k_mean,
-                              const void* workspace, size_t workspace_bytes, int q_block) {
+                              const void* workspace, size_t workspace_bytes, int q_block,
+                              int k_block) {
   if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !workspace)
     return SAGE_ERR_NULL;
   int st = check_shape(B, N, H, D);
   if (st != SAGE_OK) return st;
   if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
+  if (k_block != SAGE_K_BLOCK && k_block != SAGE_K_FINE) return SAGE_ERR_UNSUPPORTED;
   if ((st = check_strides(B, N, H, q_sb, q_sn, q_sh)) != SAGE_OK) return st;
   if ((st = check_strides(B, N, H, k_sb, k_sn, k_sh)) != SAGE_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
@@ -113,7 +115,7 @@ int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t
   if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
   const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
   const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / q_block) * 4),
-                         range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / 64) * 4),
+                         range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / k_block) * 4),
                          range_of(k_mean, bh * D * 2), range_of(workspace, need)};
   const Range ins[2] = {range_of(q, view_bytes(B, N, H, D, q_sb, q_sn, q_sh)),
                         range_of(k, view_bytes(B, N, H, D, k_sb, k_sn, k_sh))};
@@ -128,7 +130,7 @@ int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_
                            size_t workspace_bytes) {
   return sage_validate_quant_qk_ex(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8,
                                    q_scale, k_i8, k_scale, k_mean, workspace, workspace_bytes,
-                                   SAGE_Q_BLOCK);
+                                   SAGE_Q_BLOCK, SAGE_K_BLOCK);
 }
 
 int sage_validate_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
@@ -154,12 +156,13 @@ int sage_validate_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_s
 int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                               const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                               const float* v_mean, int B, int N, int H, int D, const void* out,
-                              int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block) {
+                              int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !v_mean || !out)
     return SAGE_ERR_NULL;
   int st = check_shape(B, N, H, D);
   if (st != SAGE_OK) return st;
   if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
+  if (k_block != SAGE_K_BLOCK && k_block != SAGE_K_FINE) return SAGE_ERR_UNSUPPORTED;
   if ((st = check_strides(B, N, H, o_sb, o_sn, o_sh)) != SAGE_OK) return st;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_fp8) || !aligned16(out) ||
       ((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u) ||
@@ -168,7 +171,7 @@ int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const in
   const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
   const Range outs[1] = {range_of(out, view_bytes(B, N, H, D, o_sb, o_sn, o_sh))};
   const Range ins[7] = {range_of(q_i8, bh * Np * D),      range_of(q_scale, bh * (Np / q_block) * 4),
-                        range_of(k_i8, bh * Np * D),      range_of(k_scale, bh * (Np / 64) * 4),
+                        range_of(k_i8, bh * Np * D),      range_of(k_scale, bh * (Np / k_block) * 4),
                         range_of(v_fp8, bh * D * Np),     range_of(v_scale, bh * D * 4),
                         range_of(v_mean, bh * D * 4)};
   if (any_overlap(outs, 1, ins, 7)) return SAGE_ERR_OVERLAP;
@@ -180,20 +183,21 @@ int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_
                            const float* v_mean, int B, int N, int H, int D, const void* out,
                            int64_t o_sb, int64_t o_sn, int64_t o_sh) {
   return sage_validate_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, D,
-                                   out, o_sb, o_sn, o_sh, SAGE_Q_BLOCK);
+                                   out, o_sb, o_sn, o_sh, SAGE_Q_BLOCK, SAGE_K_BLOCK);
 }
 
 int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
                      int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
                      int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
-                     void* workspace, size_t workspace_bytes, int q_block, void* stream) {
+                     void* workspace, size_t workspace_bytes, int q_block, int k_block,
+                     void* stream) {
   const int st = sage_validate_quant_qk_ex(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D,
                                            q_i8, q_scale, k_i8, k_scale, k_mean, workspace,
-                                           workspace_bytes, q_block);
+                                           workspace_bytes, q_block, k_block);
   if (st != SAGE_OK) return st;
   return status_of(sage::launch_quant_qk((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
                                          (const uint16_t*)k, B > 1 ? k_sb : 0, k_sn,
-                                         H > 1 ? k_sh : 0, B, N, H, D, q_block, q_i8, q_scale, k_i8,
+                                         H > 1 ? k_sh : 0, B, N, H, D, q_block, k_block, q_i8, q_scale, k_i8,
                                          k_scale, k_mean, workspace, (hipStream_t)stream));
 }
 
@@ -202,7 +206,8 @@ int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const
                   int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
                   void* workspace, size_t workspace_bytes, void* stream) {
   return sage_quant_qk_ex(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8, q_scale, k_i8,
-                          k_scale, k_mean, workspace, workspace_bytes, SAGE_Q_BLOCK, stream);
+                          k_scale, k_mean, workspace, workspace_bytes, SAGE_Q_BLOCK, SAGE_K_BLOCK,
+                          stream);
 }
 
 int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N, int H, int D,
@@ -219,13 +224,15 @@ int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B,
 int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                      const float* v_mean, int B, int N, int H, int D, float sm_scale, void* out,
-                     int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, void* stream) {
+                     int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block,
+                     void* stream) {
   const int st = sage_validate_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B,
-                                           N, H, D, out, o_sb, o_sn, o_sh, q_block);
+                                           N, H, D, out, o_sb, o_sn, o_sh, q_block, k_block);
   if (st != SAGE_OK) return st;
   if (!(sm_scale > 0.0f)) sm_scale = 1.0f / __builtin_sqrtf((float)D);
   return status_of(sage::launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N,
-                                         H, D, q_block, sm_scale, (uint16_t*)out, B > 1 ? o_sb : 0,
+                                         H, D, q_block, k_block, sm_scale, (uint16_t*)out,
+                                         B > 1 ? o_sb : 0,
                                          o_sn, H > 1 ? o_sh : 0, (hipStream_t)stream));
 }
 
@@ -234,7 +241,7 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                   const float* v_mean, int B, int N, int H, int D, float sm_scale, void* out,
                   int64_t o_sb, int64_t o_sn, int64_t o_sh, void* stream) {
   return sage_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, D, sm_scale,
-                          out, o_sb, o_sn, o_sh, SAGE_Q_BLOCK, stream);
+                          out, o_sb, o_sn, o_sh, SAGE_Q_BLOCK, SAGE_K_BLOCK, stream);
 }
 
 int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,

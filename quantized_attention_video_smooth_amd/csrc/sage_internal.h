@@ -59,7 +59,8 @@ inline VWorkspace v_workspace(int B, int N, int H, int D) {
 
 hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                            const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
-                           int B, int N, int H, int D, int q_block, int8_t* q_i8, float* q_scale,
+                           int B, int N, int H, int D, int q_block, int k_block, int8_t* q_i8,
+                           float* q_scale,
                            int8_t* k_i8, float* k_scale, uint16_t* k_mean, void* workspace,
                            hipStream_t stream);
 
@@ -73,7 +74,7 @@ void attn_shape(int B, int N, int H, int D, int* waves, int* workgroups);
 hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                            const float* v_mean, int B, int N, int H, int D, int q_block,
-                           float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                           int k_block, float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
                            hipStream_t stream);
 
 }  // namespace sage

@@ -171,15 +171,16 @@ __global__ __launch_bounds__(D) void finalize_kernel(
 // ---------------------------------------------------------------------------
 // Fused K centre + BF16 round + INT8 (z = 0) and Q INT8 (z = 1).
 // grid (Np/64, B*H, 2), 256 threads; one 64-token x D tile per workgroup
-// (one K block, or two 32-token Q blocks, or 64 per-token Q scales when
-// q_block == 1).  Outputs are head-major [B,H,Np,D].
+// (one K block or four 16-token K blocks when k_block == 16; two 32-token Q
+// blocks, or 64 per-token Q scales when q_block == 1).  Outputs are
+// head-major [B,H,Np,D].
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
     const uint16_t* __restrict__ q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
     const uint16_t* __restrict__ k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int H, int N, int Np,
     const uint16_t* __restrict__ k_mean, int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
-    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int q_block) {
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int q_block, int k_block) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
   constexpr int PASSES = 64 / RPP;
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
   }
 
   float x[PASSES][8];
+  float mp[PASSES];                // this thread's absmax in each pass
   float a_lo = 0.0f, a_hi = 0.0f;  // absmax of rows 0..31 and 32..63 of the tile
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
@@ -222,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[p][j]));
+    mp[p] = m;
     if (p < PASSES / 2) a_lo = fmaxf(a_lo, m); else a_hi = fmaxf(a_hi, m);
   }
   if (is_q && q_block == 1) {
@@ -249,6 +252,54 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
       if (lc == 0) q_scale[(size_t)bh * Np + t * 64 + rr] = zero ? 0.0f : a / 127.0f;
     }
     return;  // whole workgroup (is_q and q_block are uniform), before any barrier
+  }
+  if (!is_q && k_block == 16) {
+    // four K scales per 64-token tile.  The rows one wave holds in one pass
+    // (RPW consecutive rows) lie inside one 16-token block, so each block's
+    // absmax is a max over (pass, wave) pairs of per-wave maxima.
+    constexpr int RPW = 64 / LPR;
+    static_assert(RPW <= 16 && 16 % RPW == 0, "a wave's rows of a pass must sit in one block");
+    __shared__ float s16[PASSES][kThreads / 64];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const float w = wave_max(mp[p]);
+      if ((tid & 63) == 0) s16[p][tid >> 6] = w;
+    }
+    __syncthreads();
+    float inv16[4], sc16[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = 0.0f;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w)
+          if ((p * RPP + w * RPW) / 16 == j) a = fmaxf(a, s16[p][w]);
+      const float iv = 127.0f / a;
+      const bool zero = (a == 0.0f) || !__builtin_isfinite(iv);
+      inv16[j] = zero ? 0.0f : iv;
+      sc16[j] = zero ? 0.0f : a / 127.0f;
+    }
+    int8_t* dst = k_i8 + ((size_t)bh * Np + t * 64) * D + lc * 8;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int rr = lr + p * RPP, blk = rr >> 4;
+      float iv = inv16[0];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) iv = (blk == j) ? inv16[j] : iv;
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w0 |= (uint32_t)(i8_code(x[p][j] * iv) & 0xFF) << (8 * j);
+        w1 |= (uint32_t)(i8_code(x[p][j + 4] * iv) & 0xFF) << (8 * j);
+      }
+      *(uint2*)(dst + (size_t)rr * D) = make_uint2(w0, w1);
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k_scale[(size_t)bh * (Np / 16) + 4 * t + j] = sc16[j];
+    }
+    return;
   }
   a_lo = wave_max(a_lo);
   a_hi = wave_max(a_hi);
@@ -372,8 +423,9 @@ __global__ __launch_bounds__(kThreads) void v_quant_kernel(
 template <int D>
 hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                          const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
-                         int H, int q_block, int8_t* q_i8, float* q_scale, int8_t* k_i8,
-                         float* k_scale, uint16_t* k_mean, void* ws, hipStream_t stream) {
+                         int H, int q_block, int k_block, int8_t* q_i8, float* q_scale,
+                         int8_t* k_i8, float* k_scale, uint16_t* k_mean, void* ws,
+                         hipStream_t stream) {
   const StatsSplit s = stats_split(B, N, H);
   const QkWorkspace w = qk_workspace(B, N, H, D);
   char* wsb = (char*)ws;
@@ -390,7 +442,7 @@ hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t 
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((qk_quant_kernel<D>), dim3(Np / 64, B * H, 2), dim3(kThreads), 0, stream, q,
                      q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, H, N, Np, (const uint16_t*)k_mean, q_i8,
-                     q_scale, k_i8, k_scale, q_block);
+                     q_scale, k_i8, k_scale, q_block, k_block);
   return hipGetLastError();
 }
 
@@ -423,13 +475,14 @@ hipError_t quant_v_impl(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v
 
 hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                            const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
-                           int H, int D, int q_block, int8_t* q_i8, float* q_scale, int8_t* k_i8,
-                           float* k_scale, uint16_t* k_mean, void* workspace, hipStream_t stream) {
+                           int H, int D, int q_block, int k_block, int8_t* q_i8, float* q_scale,
+                           int8_t* k_i8, float* k_scale, uint16_t* k_mean, void* workspace,
+                           hipStream_t stream) {
   if (D == 128)
-    return quant_qk_impl<128>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, q_i8,
-                              q_scale, k_i8, k_scale, k_mean, workspace, stream);
-  return quant_qk_impl<64>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, q_i8, q_scale,
-                           k_i8, k_scale, k_mean, workspace, stream);
+    return quant_qk_impl<128>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, k_block,
+                              q_i8, q_scale, k_i8, k_scale, k_mean, workspace, stream);
+  return quant_qk_impl<64>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, k_block, q_i8,
+                           q_scale, k_i8, k_scale, k_mean, workspace, stream);
 }
 
 hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,

@@ -121,30 +121,40 @@ def test_workspace_sizes(sage):
     assert a % 256 == 0 and b % 256 == 0
 
 
-def test_ex_entry_points_q_block(sage):
-    """The _ex calls accept q_block 32 or 1 and refuse anything else before any
-    HIP call; q_scale's range check follows q_block."""
+def test_ex_entry_points_granularity(sage):
+    """The _ex calls accept q_block 32 or 1 and k_block 64 or 16, refuse
+    anything else before any HIP call, and size the scale ranges by them."""
     lib = sage.lib()
     B, N, H, D = 1, 100, 2, 64
     Np = 128
     big = 1 << 40
     args = [big, 0, H * D, D, 2 * big, 0, H * D, D, B, N, H, D,
             3 * big, 4 * big, 5 * big, 6 * big, 7 * big, 8 * big, 1 << 30]
-    assert lib.sage_validate_quant_qk_ex(*args, 32) == 0
-    assert lib.sage_validate_quant_qk_ex(*args, 1) == 0
+    for qb in (32, 1):
+        for kb in (64, 16):
+            assert lib.sage_validate_quant_qk_ex(*args, qb, kb) == 0
     for bad in (0, 2, 16, 64, -1):
-        assert lib.sage_validate_quant_qk_ex(*args, bad) == -3
-        assert lib.sage_quant_qk_ex(*args, bad, None) == -3
+        assert lib.sage_validate_quant_qk_ex(*args, bad, 64) == -3
+        assert lib.sage_quant_qk_ex(*args, bad, 64, None) == -3
+    for bad in (0, 1, 32, 128, -16):
+        assert lib.sage_validate_quant_qk_ex(*args, 32, bad) == -3
+        assert lib.sage_quant_qk_ex(*args, 32, bad, None) == -3
     # per-token q_scale is 32x longer: a q_scale placed just below k_i8 now overlaps it
     near = list(args)
     near[13] = 5 * big - B * H * Np * 4 // 32
-    assert lib.sage_validate_quant_qk_ex(*near, 32) == 0
-    assert lib.sage_validate_quant_qk_ex(*near, 1) == -7
+    assert lib.sage_validate_quant_qk_ex(*near, 32, 64) == 0
+    assert lib.sage_validate_quant_qk_ex(*near, 1, 64) == -7
+    # 16-token k_scale is 4x longer: one placed just below k_mean now overlaps it
+    near = list(args)
+    near[15] = 7 * big - B * H * Np * 4 // 64
+    assert lib.sage_validate_quant_qk_ex(*near, 32, 64) == 0
+    assert lib.sage_validate_quant_qk_ex(*near, 32, 16) == -7
     aargs = [big, 2 * big, 3 * big, 4 * big, 5 * big, 6 * big, 7 * big, B, N, H, D,
              8 * big, N * H * D, H * D, D]
-    assert lib.sage_validate_attn_fwd_ex(*aargs, 1) == 0
-    assert lib.sage_validate_attn_fwd_ex(*aargs, 8) == -3
-    assert lib.sage_attn_fwd_ex(*aargs[:11], 0.0, *aargs[11:], 8, None) == -3
+    assert lib.sage_validate_attn_fwd_ex(*aargs, 1, 16) == 0
+    assert lib.sage_validate_attn_fwd_ex(*aargs, 8, 64) == -3
+    assert lib.sage_validate_attn_fwd_ex(*aargs, 32, 32) == -3
+    assert lib.sage_attn_fwd_ex(*aargs[:11], 0.0, *aargs[11:], 8, 64, None) == -3
 
 
 def test_attn_launch_shape(sage):

@@ -38,10 +38,10 @@ def sage():
     return s
 
 
-def _gpu_quant(sage, q, k, v, q_block=32):
+def _gpu_quant(sage, q, k, v, q_block=32, k_block=64):
     dev = torch.device("cuda")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    qk = sage.quant_qk(qd, kd, q_block=q_block)
+    qk = sage.quant_qk(qd, kd, q_block=q_block, k_block=k_block)
     vq = sage.quant_v(vd)
     torch.cuda.synchronize()
     return qd, kd, vd, qk, vq
@@ -50,13 +50,14 @@ def _gpu_quant(sage, q, k, v, q_block=32):
 def _check_quant_bits(qk, vq, ref_qk, ref_v, N):
     q_i8, q_scale, k_i8, k_scale, k_mean = [t.cpu() for t in qk]
     v_fp8, v_scale, v_mean = [t.cpu() for t in vq]
-    nq, nk = math.ceil(N / ref_qk.get("q_block", 32)), math.ceil(N / 64)
+    nq, nk = math.ceil(N / ref_qk.get("q_block", 32)), math.ceil(N / ref_qk.get("k_block", 64))
     np.testing.assert_array_equal(q_i8[:, :, :N].numpy(), ref_qk["q_i8"])
     np.testing.assert_array_equal(k_i8[:, :, :N].numpy(), ref_qk["k_i8"])
     assert torch.all(q_i8[:, :, N:] == 0) and torch.all(k_i8[:, :, N:] == 0)
     np.testing.assert_array_equal(q_scale[:, :, :nq].numpy().view(np.uint32), ref_qk["q_scale"].view(np.uint32))
     assert torch.all(q_scale[:, :, nq:] == 0)
     np.testing.assert_array_equal(k_scale[:, :, :nk].numpy().view(np.uint32), ref_qk["k_scale"].view(np.uint32))
+    assert torch.all(k_scale[:, :, nk:] == 0)
     np.testing.assert_array_equal(k_mean.view(torch.int16).numpy().view(np.uint16), ref_qk["k_mean"])
     np.testing.assert_array_equal(v_fp8.numpy(), ref_v["v_fp8"])
     np.testing.assert_array_equal(v_scale.numpy().view(np.uint32), ref_v["v_scale"].view(np.uint32))
@@ -237,14 +238,15 @@ def test_quant_single_long_head(sage):
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
 
 
+@pytest.mark.parametrize("k_block", [64, 16])
 @pytest.mark.parametrize("D", [64, 128])
-def test_degenerate_inputs(sage, D):
+def test_degenerate_inputs(sage, D, k_block):
     """Zero and subnormal quantisation blocks (scale 0, codes 0 through the
     zero guard when 127/a or 448/a overflows), a head with constant K (all
     scores 0: uniform attention) and a constant V channel (scale 0: the output
     channel is bf16(v_mean) exactly)."""
     cfg = synth.custom(2, 200, 3, D, tag=312)
-    _log(f"[parity] degenerate inputs B{cfg.B} N{cfg.N} H{cfg.H} D{D}")
+    _log(f"[parity] degenerate inputs B{cfg.B} N{cfg.N} H{cfg.H} D{D} k_block {k_block}")
     q, k, v = synth.make_qkv(cfg)
     tiny = torch.tensor(1e-40, dtype=torch.bfloat16)          # a bf16 subnormal
     assert 0 < float(tiny) < 1.2e-38
@@ -254,12 +256,12 @@ def test_degenerate_inputs(sage, D):
     v[:, :, 1, 7] = 2.5                                       # a constant V channel
     sign = torch.where(torch.arange(cfg.N) % 2 == 0, 1.0, -1.0).to(torch.bfloat16)
     v[:, :, 0, 3] = tiny * sign[None, :]                      # a V channel of +-subnormals
-    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    ref_qk, ref_v = oracle.quant_qk(q, k, k_block=k_block), oracle.quant_v(v)
     assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
     assert np.all(ref_qk["q_scale"][:, :, 1] == 0) and np.all(ref_qk["q_scale"][:, 0, 2] == 0)
     assert np.all(ref_qk["k_scale"][:, 2] == 0)
     assert np.all(ref_v["v_scale"][:, 1, 7] == 0) and np.all(ref_v["v_scale"][:, 0, 3] == 0)
-    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v)
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v, k_block=k_block)
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
     out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
     torch.cuda.synchronize()
@@ -275,51 +277,58 @@ def test_degenerate_inputs(sage, D):
     assert torch.equal(o2, o2[:, :1].expand_as(o2))
 
 
-PER_TOKEN = [
+GRAN_SHAPES = [
     synth.config(0),
     synth.custom(2, 63, 3, 64, tag=302),
+    # N = 65 and 200: the last key tile holds 16-key blocks wholly beyond N
+    synth.custom(1, 65, 2, 128, tag=303),
     synth.custom(3, 200, 2, 128, tag=304),
     synth.custom(1, 777, 4, 128, tag=305),
 ]
+GRANS = [(1, 64), (32, 16), (1, 16)]
 
 
-@pytest.mark.parametrize("cfg", PER_TOKEN, ids=lambda c: f"{c.name}-B{c.B}N{c.N}H{c.H}D{c.D}")
-def test_per_token_q_full(sage, cfg):
-    """One Q scale per token (q_block 1): codes and scales bit-exact against the
-    oracle's per-token quantiser, K and V outputs identical to the per-block
-    run, attention within the oracle bar."""
-    _log(f"[parity] per-token Q {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
+@pytest.mark.parametrize("qb,kb", GRANS, ids=lambda g: str(g))
+@pytest.mark.parametrize("cfg", GRAN_SHAPES, ids=lambda c: f"{c.name}-B{c.B}N{c.N}H{c.H}D{c.D}")
+def test_granularity_full(sage, cfg, qb, kb):
+    """One Q scale per token (q_block 1) and/or four K scales per key tile
+    (k_block 16): codes and scales bit-exact against the oracle at the same
+    granularity, the other tensor identical to the default run, attention
+    within the oracle bar."""
+    _log(f"[parity] q_block {qb} k_block {kb} {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
     q, k, v = synth.make_qkv(cfg)
-    ref_qk, ref_v = oracle.quant_qk(q, k, q_block=1), oracle.quant_v(v)
+    ref_qk, ref_v = oracle.quant_qk(q, k, q_block=qb, k_block=kb), oracle.quant_v(v)
     assert ref_qk["inexact"] == 0 and ref_v["bad"] == 0
-    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v, q_block=1)
-    assert qk[1].shape[-1] == qk[0].shape[2]
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v, q_block=qb, k_block=kb)
+    assert qk[1].shape[-1] == qk[0].shape[2] // qb and qk[3].shape[-1] == qk[2].shape[2] // kb
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
-    qk32 = sage.quant_qk(qd, kd)
+    dflt = sage.quant_qk(qd, kd)
     torch.cuda.synchronize()
-    for a, b in zip(qk[2:], qk32[2:]):
-        assert torch.equal(a, b)
+    same = ([0, 1] if qb == 32 else []) + ([2, 3] if kb == 64 else []) + [4]
+    for i in same:
+        assert torch.equal(qk[i], dflt[i])
     out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
     torch.cuda.synchronize()
     got = _rows_gathered(out, np.arange(cfg.N))
     tiled = oracle.attn_tiled(ref_qk, ref_v)
     exact = oracle.attn_exact(q, k, v)
     e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
-    e_blk = oracle.rel_l2(oracle.attn_tiled(oracle.quant_qk(q, k), ref_v), exact)
+    e_dflt = oracle.rel_l2(oracle.attn_tiled(oracle.quant_qk(q, k), ref_v), exact)
     _log(f"  rel L2: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}  "
-         f"per-block-oracle-vs-exact {e_blk:.3e}")
+         f"default-oracle-vs-exact {e_dflt:.3e}")
     assert e_or <= TOL_ORACLE
-    assert e_ex <= max(TOL_EXACT, e_blk + TOL_ORACLE)
+    assert e_ex <= max(TOL_EXACT, e_dflt + TOL_ORACLE)
 
 
-def test_per_token_q_workload_sampled(sage):
-    """FLUX joint shape with per-token Q scales: quantised outputs bit-exact in
-    full, attention on every 16th query row."""
+@pytest.mark.parametrize("qb,kb", GRANS, ids=lambda g: str(g))
+def test_granularity_workload_sampled(sage, qb, kb):
+    """FLUX joint shape at the finer granularities: quantised outputs bit-exact
+    in full, attention on every 16th query row."""
     cfg = synth.config(1)
-    _log(f"[parity] per-token Q workload {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
+    _log(f"[parity] q_block {qb} k_block {kb} workload {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
     q, k, v = synth.make_qkv(cfg)
-    ref_qk, ref_v = oracle.quant_qk(q, k, q_block=1), oracle.quant_v(v)
-    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v, q_block=1)
+    ref_qk, ref_v = oracle.quant_qk(q, k, q_block=qb, k_block=kb), oracle.quant_v(v)
+    qd, kd, vd, qk, vq = _gpu_quant(sage, q, k, v, q_block=qb, k_block=kb)
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
     out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
     torch.cuda.synchronize()

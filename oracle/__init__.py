@@ -38,6 +38,7 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int
 _dbl = ctypes.c_double
+_f32 = ctypes.c_float
 
 
 def _load():
@@ -68,6 +69,7 @@ def _load():
                             _i32, _i32, _vp, _i32, _vp], None),
         "orc_attn_exact": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                             _i32, _i32, _i32, _i32, _dbl, _vp, _i32, _vp], None),
+        "orc_norm_rope": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp], _i32),
         "orc_num_threads": ([], _i32),
     }
     for name, (args, res) in sig.items():
@@ -156,6 +158,24 @@ def quant_qk(q, k, q_block: int = BQ, k_block: int = BK):
     out["q_block"] = q_block
     out["k_block"] = k_block
     return out
+
+
+def norm_rope(x, weight, rope, eps: float = 1e-6):
+    """QK RMSNorm + RoPE producer (orc_norm_rope).  x bf16 torch CPU [B,N,H,D]
+    (any strides, d-stride 1), weight bf16 [D], rope fp32 [N, D/2, 2] (cos, sin).
+    Returns (y bf16 torch tensor [B,N,H,D] contiguous, number of rows whose
+    sum of squares is not provably exact)."""
+    import torch
+    B, N, H, D = x.shape
+    xb, sb, sn, sh = _bf16_view(x)
+    w = np.ascontiguousarray(weight.contiguous().view(torch.int16).numpy())
+    assert w.shape == (D,)
+    rope = np.ascontiguousarray(rope, dtype=np.float32)
+    assert rope.shape == (N, D // 2, 2)
+    y = torch.empty((B, N, H, D), dtype=torch.bfloat16)
+    yb = y.view(torch.int16).numpy()
+    bad = _load().orc_norm_rope(_p(xb), sb, sn, sh, B, N, H, D, _p(w), float(eps), _p(rope), _p(yb))
+    return y, int(bad)
 
 
 def k_mean(k):

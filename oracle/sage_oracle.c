@@ -17,6 +17,8 @@
  *   [M]  "MiniMax H3 on DGX Spark": §01 precision map (Sage2++ is QK INT8 / PV FP8).
  *   [F]  "Why can an A10 run FLUX.1" article, §1.1: E4M3 = 1 sign, 4 exponent,
  *        3 mantissa bits.
+ *   [S]  "FLUX 3 Action" SGLang page: §1 (4-axis (t, h, w, l) RoPE in the joint
+ *        blocks) and the latency notes (QK RMSNorm + RoPE as one fused kernel).
  * Where the pages leave a step open, the reading used is stated at the step.
  * All non-codec arithmetic is fp64 unless a step fixes fp32 (the quantiser
  * rules are fp32 operations, so both sides take the same integer decisions).
@@ -228,6 +230,62 @@ void orc_quant_i8_blocks(const uint16_t* x, int64_t sb, int64_t sn, int64_t sh, 
             codes[(((int64_t)b * H + h) * N + j) * D + d] = (int8_t)c;
           }
       }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Producer of Q and K: QK RMSNorm + RoPE                                     */
+/* ------------------------------------------------------------------------- */
+
+/* The fused QK RMSNorm + RoPE of the "FLUX 3 Action" SGLang page (§1: a 4-axis
+ * (t, h, w, l) RoPE; latency notes: the fused kernel sits at bf16 rounding
+ * level) whose BF16 NHD result feeds the quantiser (report card B).  Reading:
+ * the eager composition with each bf16 rounding kept.  For token row x of a
+ * head (D channels), with per-channel weights w (bf16) and the rotation table
+ * rope[token][pair] = (c, s) (fp32):
+ *   ms    = (sum_d x_d^2) / D           fp64
+ *   r     = fp32(1 / sqrt(ms + eps))    fp64 add, sqrt and divide, then fp32
+ *   n_d   = bf16(x_d * r)               fp32 product
+ *   u_d   = bf16(n_d * w_d)             fp32 product of two bf16 values (exact)
+ *   y_2i  = bf16(u_2i * c - u_2i+1 * s) fp32: both products rounded, then the
+ *   y_2i+1= bf16(u_2i * s + u_2i+1 * c) difference / sum rounded
+ * The fp64 sum of squares is exact when every x_d^2 is a multiple of u^2 (u
+ * the smallest bf16 ulp among the row's non-zero values, always true) and
+ * sum x_d^2 < u^2 2^53; it then does not depend on summation order.
+ * x strided [B][N][H][D]; y contiguous [B][N][H][D] (bf16 bits).
+ * Returns the number of rows whose sum is not provably exact. */
+int orc_norm_rope(const uint16_t* x, int64_t sb, int64_t sn, int64_t sh, int B, int N, int H, int D,
+                  const uint16_t* w, float eps, const float* rope, uint16_t* y) {
+  int bad = 0;
+#pragma omp parallel for collapse(2) reduction(+ : bad) schedule(static)
+  for (int b = 0; b < B; ++b)
+    for (int n = 0; n < N; ++n)
+      for (int h = 0; h < H; ++h) {
+        const uint16_t* row = &AT(x, b, n, h, sb, sn, sh);
+        uint16_t* out = y + (((int64_t)b * N + n) * H + h) * D;
+        double ss = 0.0, umin = INFINITY;
+        for (int d = 0; d < D; ++d) {
+          double v = (double)orc_bf16_value(row[d]);
+          ss += v * v;
+          if (v != 0.0) {
+            double u = bf16_ulp(row[d]);
+            if (u < umin) umin = u;
+          }
+        }
+        if (umin != INFINITY && !(ss < ldexp(umin * umin, 53))) bad += 1;
+        const double ms = ss / (double)D;
+        const float r = (float)(1.0 / sqrt(ms + (double)eps));
+        for (int i = 0; i < D / 2; ++i) {
+          float u0 = orc_bf16_value(orc_bf16_round(orc_bf16_value(row[2 * i]) * r));
+          float u1 = orc_bf16_value(orc_bf16_round(orc_bf16_value(row[2 * i + 1]) * r));
+          u0 = orc_bf16_value(orc_bf16_round(u0 * orc_bf16_value(w[2 * i])));
+          u1 = orc_bf16_value(orc_bf16_round(u1 * orc_bf16_value(w[2 * i + 1])));
+          const float c = rope[((int64_t)n * (D / 2) + i) * 2], s = rope[((int64_t)n * (D / 2) + i) * 2 + 1];
+          const float a0 = u0 * c, a1 = u1 * s, b0 = u0 * s, b1 = u1 * c;
+          out[2 * i] = orc_bf16_round(a0 - a1);
+          out[2 * i + 1] = orc_bf16_round(b0 + b1);
+        }
+      }
+  return bad;
 }
 
 /* Steps 1-4 as ONE routine (the fused form the report describes in card A:

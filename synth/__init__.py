@@ -18,6 +18,13 @@ synthetic recipe, N(mean, variance)):
 
 Per-channel offsets and outlier multipliers are indexed by (h, d) and shared by
 every batch entry and token.
+
+Inputs of the QK RMSNorm + RoPE producer ("FLUX 3 Action" SGLang page, §1 and
+the latency notes: a fused QK RMSNorm + RoPE over a 4-axis (t, h, w, l) RoPE):
+the pre-norm Q and K are the tensors above; `norm_weight` draws the per-channel
+weights 1 + 0.1 z (bf16); `rope_table` builds the cos / sin of each token's
+rotation angles from a synthetic 4-axis position grid (the pages give neither
+the axis sizes nor the frequencies; see the function).
 """
 from __future__ import annotations
 
@@ -37,6 +44,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
 STREAM_K_OFF, STREAM_V_OFF, STREAM_Q_OFF = 4, 5, 6
 STREAM_OUTLIER = 7
+STREAM_QW, STREAM_KW = 8, 9
 
 
 def build() -> str:
@@ -193,3 +201,48 @@ def query_subset(N: int, every: int = 8, block: int = 32) -> np.ndarray:
     blocks = sorted(set(range(0, nblk, every)) | {nblk - 1})
     rows = [r for b in blocks for r in range(b * block, min(N, (b + 1) * block))]
     return np.asarray(rows, dtype=np.int32)
+
+
+def norm_weight(cfg, which: str, seed: int = 0):
+    """RMSNorm weight of the Q ('q') or K ('k') norm: bf16 torch tensor [D],
+    1 + 0.1 z, shared by every head."""
+    import torch
+    if not isinstance(cfg, Config):
+        cfg = config(cfg)
+    stream = {"q": STREAM_QW, "k": STREAM_KW}[which]
+    w = 1.0 + 0.1 * normals(seed, cfg.idx, stream, cfg.D)
+    return torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16)
+
+
+def rope_positions(N: int) -> np.ndarray:
+    """Synthetic 4-axis positions [N, 4] = (t, h, w, l) of a joint sequence: the
+    first min(512, N // 8) tokens are text (t = h = w = 0, l = index), the rest
+    are video latents on a t x 16 x 32 grid (l = 0)."""
+    n_text = min(512, N // 8)
+    pos = np.zeros((N, 4), np.int64)
+    pos[:n_text, 3] = np.arange(n_text)
+    j = np.arange(N - n_text)
+    pos[n_text:, 0] = j // 512
+    pos[n_text:, 1] = (j // 32) % 16
+    pos[n_text:, 2] = j % 32
+    return pos
+
+
+def rope_table(N: int, D: int, theta: float = 10000.0) -> np.ndarray:
+    """cos / sin of the rotation angles: fp32 [N, D/2, 2].  The D/2 channel pairs
+    are split over the axes (t, h, w, l) as (1, 3, 3, 1) eighths; pair i of an
+    axis with d pairs turns at pos * theta^(-i/d).  Angles and cos / sin are fp64,
+    rounded once to fp32."""
+    P = D // 2
+    split = [P // 8, 3 * P // 8, 3 * P // 8, P // 8]
+    pos = rope_positions(N).astype(np.float64)
+    ang = np.empty((N, P), np.float64)
+    c0 = 0
+    for a, d in enumerate(split):
+        freq = theta ** (-np.arange(d, dtype=np.float64) / d)
+        ang[:, c0:c0 + d] = pos[:, a:a + 1] * freq[None, :]
+        c0 += d
+    out = np.empty((N, P, 2), np.float32)
+    out[..., 0] = np.cos(ang)
+    out[..., 1] = np.sin(ang)
+    return out

@@ -110,6 +110,11 @@ def main():
                     help="Q scale granularity: one scale per 32-token block (default) or per token")
     ap.add_argument("--k-block", type=int, choices=[64, 16], default=64,
                     help="K scale granularity: one scale per 64-token key tile (default) or per 16 tokens")
+    ap.add_argument("--producer", choices=["none", "fused", "composed"], default="none",
+                    help="inputs are pre-norm Q and K of a QK RMSNorm + RoPE producer: 'fused' runs "
+                         "sage_norm_rope_quant_qk, 'composed' runs sage_norm_rope on Q and on K "
+                         "(bf16 NHD stores) and then sage_quant_qk_ex; 'none' (default) quantises "
+                         "Q and K as given")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the run, copy 256 MiB device to device once: a kernel of known "
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counter readings")
@@ -145,12 +150,44 @@ def main():
     v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     v_mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
-    ws_qk = torch.empty(sage.sage_quant_qk_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
+    ws_qk = torch.empty(max(sage.sage_quant_qk_workspace_size(B, N, H, D),
+                            sage.sage_norm_rope_quant_qk_workspace_size(B, N, H, D)),
+                        dtype=torch.uint8, device=dev)
     ws_v = torch.empty(sage.sage_quant_v_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
     qs, ks, vs, os_ = q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3]
     do_attn = args.workload != "quant_long"
+    prod = args.producer
+    if prod != "none":
+        wq = synth.norm_weight(cfg, "q").to(dev)
+        wk = synth.norm_weight(cfg, "k").to(dev)
+        rope = torch.from_numpy(synth.rope_table(N, D)).to(dev)
+        yq = torch.empty_like(q)
+        yk = torch.empty_like(k)
+        eps = 1e-6
+
+    def qk_call(sp_):
+        """The Q/K segment of a step: the quantiser, with the producer in front
+        of it when --producer is given."""
+        if prod == "fused":
+            return lib.sage_norm_rope_quant_qk(
+                q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, wq.data_ptr(), wk.data_ptr(),
+                rope.data_ptr(), eps, q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
+                k_scale.data_ptr(), k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp_)
+        src_q, src_k = q, k
+        st_ = 0
+        if prod == "composed":
+            st_ |= lib.sage_norm_rope(q.data_ptr(), *qs, B, N, H, D, wq.data_ptr(), rope.data_ptr(),
+                                      eps, yq.data_ptr(), *yq.stride()[:3], sp_)
+            st_ |= lib.sage_norm_rope(k.data_ptr(), *ks, B, N, H, D, wk.data_ptr(), rope.data_ptr(),
+                                      eps, yk.data_ptr(), *yk.stride()[:3], sp_)
+            src_q, src_k = yq, yk
+        st_ |= lib.sage_quant_qk_ex(src_q.data_ptr(), *src_q.stride()[:3], src_k.data_ptr(),
+                                    *src_k.stride()[:3], B, N, H, D, q_i8.data_ptr(),
+                                    q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
+                                    k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp_)
+        return st_
 
     side = torch.cuda.Stream(device=dev)  # default priority
     side_p = int(side.cuda_stream)
@@ -162,9 +199,7 @@ def main():
         side.wait_event(ev_in[0])
         st = lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
                               v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), side_p)
-        st |= lib.sage_quant_qk_ex(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, q_i8.data_ptr(),
-                                q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
-                                k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp)
+        st |= qk_call(sp)
         ev_in[1].record(side)
         stream.wait_event(ev_in[1])
         if do_attn:
@@ -180,9 +215,7 @@ def main():
             return
         if evs:
             evs[0].record(stream)
-        st = lib.sage_quant_qk_ex(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, q_i8.data_ptr(),
-                               q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
-                               k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp)
+        st = qk_call(sp)
         if evs:
             evs[1].record(stream)
         st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
@@ -228,6 +261,10 @@ def main():
     p90 = {k2: sorted(v2)[min(len(v2) - 1, (9 * len(v2)) // 10)] for k2, v2 in per.items()}
 
     work = algorithmic(B, N, H, D, qb, kbl)
+    if prod != "none":
+        # the rotation table, read once per step (the weights are negligible);
+        # the Q/K segment's bytes are otherwise those of the quantiser
+        work["quant_q_bytes"] += 4.0 * N * D
     waves, wgs = sage.sage_attn_launch_shape(B, N, H, D)
     step_s = ms_per_step * 1e-3
     if do_attn:
@@ -269,7 +306,8 @@ def main():
         "data": "synthetic (seeded counter-based normals, bf16 NHD)",
         "config": {"workload": cfg.name, "B": B, "N": N, "H": H, "D": D, "causal": False,
                    "layout": "NHD bf16 in, bf16 out", "seed": args.seed,
-                   "streams": args.streams, "q_block": qb, "k_block": kbl},
+                   "streams": args.streams, "q_block": qb, "k_block": kbl,
+                   "producer": prod},
         "kernels_ms": {k2: {"avg": round(avg[k2], 5), "median": round(med[k2], 5),
                             "min": round(mn[k2], 5), "p90": round(p90[k2], 5)} for k2 in per},
         "attn_tflops": round(work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12, 2) if do_attn else None,

@@ -12,6 +12,8 @@
  *     the V+MLP projection; tiled transpose, padding and permutation).
  *   "MiniMax H3 on DGX Spark", §01 precision map (QK INT8 / PV FP8).
  *   "Why can an A10 run FLUX.1", §1.1 (E4M3: 4 exponent, 3 mantissa bits).
+ *   "FLUX 3 Action" SGLang page: §1 (4-axis (t, h, w, l) RoPE in the joint
+ *     blocks) and the latency notes (QK RMSNorm + RoPE as one fused kernel).
  *
  * Conventions shared by every entry point
  *   - Tensors named "[B,N,H,D]" are bf16 (uint16 bit patterns) in token-major
@@ -52,7 +54,8 @@ enum sage_status {
   SAGE_ERR_ALIGN = -5,       /* a pointer or stride breaks 16-byte alignment     */
   SAGE_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required       */
   SAGE_ERR_OVERLAP = -7,     /* an output overlaps an input or another output    */
-  SAGE_ERR_HIP = -8          /* a HIP launch or runtime call failed              */
+  SAGE_ERR_HIP = -8,         /* a HIP launch or runtime call failed              */
+  SAGE_ERR_VALUE = -9        /* a scalar argument is out of range (e.g. eps)     */
 };
 
 #define SAGE_BQ 32          /* Q quantisation block, tokens (one MFMA column tile) */
@@ -99,6 +102,9 @@ int sage_v_slot(int t);
  * contents on entry; clobbered by the call.  One workspace must not be shared
  * by calls that may run concurrently.  Returns 0 for unsupported shapes. */
 size_t sage_quant_qk_workspace_size(int B, int N, int H, int D);
+/* Workspace bytes of sage_norm_rope_quant_qk: those of sage_quant_qk plus one
+ * fp32 per K token row (B*H*Np*4, rounded up to 256); 0 for unsupported sizes. */
+size_t sage_norm_rope_quant_qk_workspace_size(int B, int N, int H, int D);
 size_t sage_quant_v_workspace_size(int B, int N, int H, int D);
 
 /*
@@ -152,6 +158,50 @@ int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                      int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
                      void* workspace, size_t workspace_bytes, int q_block, int k_block,
                      void* stream);
+
+/*
+ * sage_norm_rope -- the QK RMSNorm + RoPE producer of Q or K ("FLUX 3 Action"
+ * SGLang page: a fused QK RMSNorm + RoPE, 4-axis RoPE), storing BF16 NHD
+ * directly (report card B).  Per token row x of a head, with weights w and
+ * (c, s) = rope[token][pair] for channel pair (2i, 2i+1):
+ *   r      = fp32( 1 / sqrt(sum_d x_d^2 / D + eps) )   fp64 sum, add, sqrt, divide
+ *   u_d    = bf16( bf16(x_d * r) * w_d )                fp32 products
+ *   y_2i   = bf16( u_2i * c - u_2i+1 * s )              fp32: products, then sum
+ *   y_2i+1 = bf16( u_2i * s + u_2i+1 * c )
+ * i.e. the eager composition with each of its bf16 roundings kept.  The fp64
+ * sum of squares is exact, and so independent of reduction order, when
+ * sum_d x_d^2 < u^2 * 2^53 for u the smallest bf16 ulp among the row's
+ * non-zero values (a row of O(1) values holding a value below ~2^-20 of
+ * them can break it; the result then still differs from the exact one only
+ * through the fp64 rounding of that sum).
+ * Inputs (device): x bf16 [B,N,H,D] (strided); w bf16 [D]; rope fp32
+ * [N][D/2][2] = (cos, sin), the same for every batch entry and head; eps
+ * finite and >= 0 (else SAGE_ERR_VALUE).  w and rope 16-byte aligned.
+ * Output (device): y bf16 [B,N,H,D] with element strides (y_sb, y_sn, y_sh),
+ * unit d-stride; it must not overlap x, w or rope.
+ */
+int sage_norm_rope(const void* x, int64_t x_sb, int64_t x_sn, int64_t x_sh,
+                   int B, int N, int H, int D,
+                   const uint16_t* w, const float* rope, float eps,
+                   void* y, int64_t y_sb, int64_t y_sn, int64_t y_sh, void* stream);
+
+/*
+ * sage_norm_rope_quant_qk -- the producer fused into the quantiser: takes the
+ * pre-norm Q and K, applies sage_norm_rope to each (weights wq and wk, the
+ * same rope table and eps) while loading, and writes what sage_quant_qk_ex
+ * writes for the producer's BF16 outputs, bit for bit, without storing them.
+ * K is read twice (its mean needs the whole head), Q once.
+ * Arguments: those of sage_quant_qk_ex plus wq, wk, rope and eps, checked as
+ * for sage_norm_rope; the workspace is sage_norm_rope_quant_qk_workspace_size
+ * bytes (it also carries each K row's r from the first K pass to the second).
+ */
+int sage_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                            const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                            int B, int N, int H, int D,
+                            const uint16_t* wq, const uint16_t* wk, const float* rope, float eps,
+                            int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                            uint16_t* k_mean, void* workspace, size_t workspace_bytes,
+                            int q_block, int k_block, void* stream);
 
 /*
  * sage_quant_v -- V smoothing + FP8 E4M3 V, transposed, padded and permuted
@@ -253,6 +303,19 @@ int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
                               int B, int N, int H, int D,
                               const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
                               int q_block, int k_block);
+
+int sage_validate_norm_rope(const void* x, int64_t x_sb, int64_t x_sn, int64_t x_sh,
+                            int B, int N, int H, int D,
+                            const uint16_t* w, const float* rope, float eps,
+                            const void* y, int64_t y_sb, int64_t y_sn, int64_t y_sh);
+int sage_validate_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                                     const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                                     int B, int N, int H, int D,
+                                     const uint16_t* wq, const uint16_t* wk, const float* rope,
+                                     float eps, const int8_t* q_i8, const float* q_scale,
+                                     const int8_t* k_i8, const float* k_scale,
+                                     const uint16_t* k_mean, const void* workspace,
+                                     size_t workspace_bytes, int q_block, int k_block);
 
 /* Static, never-NULL description of a status code. */
 const char* sage_status_string(int status);

@@ -41,6 +41,7 @@ _SIGS = {
     "sage_v_slot": ([_i32], _i32),
     "sage_quant_qk_workspace_size": ([_i32] * 4, _sz),
     "sage_quant_v_workspace_size": ([_i32] * 4, _sz),
+    "sage_norm_rope_quant_qk_workspace_size": ([_i32] * 4, _sz),
     "sage_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "sage_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -58,6 +59,16 @@ _SIGS = {
                           _vp, _i64, _i64, _i64, _i32, _i32, _vp], _i32),
     "sage_validate_quant_qk_ex": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
                                    _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32], _i32),
+    "sage_norm_rope": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _f32,
+                        _vp, _i64, _i64, _i64, _vp], _i32),
+    "sage_validate_norm_rope": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _f32,
+                                 _vp, _i64, _i64, _i64], _i32),
+    "sage_norm_rope_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                 _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                 _i32, _i32, _vp], _i32),
+    "sage_validate_norm_rope_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32,
+                                          _i32, _i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
+                                          _vp, _vp, _vp, _sz, _i32, _i32], _i32),
     "sage_validate_attn_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                    _vp, _i64, _i64, _i64, _i32, _i32], _i32),
     "sage_status_string": ([_i32], ctypes.c_char_p),
@@ -114,6 +125,14 @@ def sage_attn_fwd_ex(*args) -> int:
     return lib().sage_attn_fwd_ex(*args)
 
 
+def sage_norm_rope(*args) -> int:
+    return lib().sage_norm_rope(*args)
+
+
+def sage_norm_rope_quant_qk(*args) -> int:
+    return lib().sage_norm_rope_quant_qk(*args)
+
+
 def sage_attn_launch_shape(B: int, N: int, H: int, D: int) -> tuple:
     """(waves per workgroup, workgroups) of the attention launch for these sizes."""
     w, g = ctypes.c_int(0), ctypes.c_int(0)
@@ -136,6 +155,10 @@ def sage_quant_qk_workspace_size(B: int, N: int, H: int, D: int) -> int:
 
 def sage_quant_v_workspace_size(B: int, N: int, H: int, D: int) -> int:
     return lib().sage_quant_v_workspace_size(B, N, H, D)
+
+
+def sage_norm_rope_quant_qk_workspace_size(B: int, N: int, H: int, D: int) -> int:
+    return lib().sage_norm_rope_quant_qk_workspace_size(B, N, H, D)
 
 
 # ---- tensor-level helpers ---------------------------------------------------
@@ -166,6 +189,61 @@ def _nhd(t, name):
     if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1 or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA bf16 [B,N,H,D] tensor with unit stride over D")
     return t.stride(0), t.stride(1), t.stride(2)
+
+
+def _producer_consts(w_list, rope, N, D):
+    import torch
+    for w in w_list:
+        if w.dtype != torch.bfloat16 or tuple(w.shape) != (D,) or not w.is_cuda or not w.is_contiguous():
+            raise ValueError("norm weights must be contiguous CUDA bf16 [D] tensors")
+    if (rope.dtype != torch.float32 or tuple(rope.shape) != (N, D // 2, 2) or not rope.is_cuda
+            or not rope.is_contiguous()):
+        raise ValueError("rope must be a contiguous CUDA fp32 [N, D/2, 2] tensor of (cos, sin)")
+
+
+def norm_rope(x, weight, rope, eps: float = 1e-6, out=None, stream=None):
+    """QK RMSNorm + RoPE producer: x bf16 [B,N,H,D] -> bf16 [B,N,H,D] (or fills `out`).
+    weight bf16 [D]; rope fp32 [N, D/2, 2] (cos, sin)."""
+    import torch
+    B, N, H, D = x.shape
+    xs = _nhd(x, "x")
+    _producer_consts([weight], rope, N, D)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=x.device)
+    ys = _nhd(out, "out")
+    _check(sage_norm_rope(x.data_ptr(), *xs, B, N, H, D, weight.data_ptr(), rope.data_ptr(),
+                          float(eps), out.data_ptr(), *ys, _stream_ptr(stream)), "sage_norm_rope")
+    return out
+
+
+def norm_rope_quant_qk(q, k, wq, wk, rope, eps: float = 1e-6, stream=None, q_block: int = 32,
+                       k_block: int = 64):
+    """The producer fused into the quantiser: pre-norm q, k bf16 [B,N,H,D] -> the outputs of
+    quant_qk(norm_rope(q, wq, rope), norm_rope(k, wk, rope)), without storing the bf16 tensors."""
+    import torch
+    B, N, H, D = q.shape
+    if tuple(k.shape) != (B, N, H, D):
+        raise ValueError("q and k must have the same shape")
+    if q_block not in (1, BQ) or k_block not in (16, 64):
+        raise ValueError("q_block must be 32 or 1 and k_block 64 or 16")
+    qs, ks = _nhd(q, "q"), _nhd(k, "k")
+    _producer_consts([wq, wk], rope, N, D)
+    Np = sage_padded_tokens(N)
+    dev = q.device
+    q_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+    q_scale = torch.empty((B, H, Np // q_block), dtype=torch.float32, device=dev)
+    k_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+    k_scale = torch.empty((B, H, Np // k_block), dtype=torch.float32, device=dev)
+    k_mean = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    need = sage_norm_rope_quant_qk_workspace_size(B, N, H, D)
+    ws = workspace(dev, need)
+    _check(sage_norm_rope_quant_qk(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D,
+                                   wq.data_ptr(), wk.data_ptr(), rope.data_ptr(), float(eps),
+                                   q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
+                                   k_scale.data_ptr(), k_mean.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   q_block, k_block, _stream_ptr(stream)),
+           "sage_norm_rope_quant_qk")
+    return q_i8, q_scale, k_i8, k_scale, k_mean
 
 
 def quant_qk(q, k, stream=None, q_block: int = 32, k_block: int = 64):

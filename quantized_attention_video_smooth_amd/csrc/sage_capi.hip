@@ -63,6 +63,37 @@ bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
+// Checks shared by sage_quant_qk_ex and sage_norm_rope_quant_qk (nr): the
+// workspace requirement differs.
+int validate_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+                int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
+                const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                const uint16_t* k_mean, const void* workspace, size_t workspace_bytes, int q_block,
+                int k_block, bool nr) {
+  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !workspace)
+    return SAGE_ERR_NULL;
+  int st = check_shape(B, N, H, D);
+  if (st != SAGE_OK) return st;
+  if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
+  if (k_block != SAGE_K_BLOCK && k_block != SAGE_K_FINE) return SAGE_ERR_UNSUPPORTED;
+  if ((st = check_strides(B, N, H, q_sb, q_sn, q_sh)) != SAGE_OK) return st;
+  if ((st = check_strides(B, N, H, k_sb, k_sn, k_sh)) != SAGE_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
+      !aligned16(k_mean) || !aligned16(workspace) || ((uintptr_t)q_scale & 3u) ||
+      ((uintptr_t)k_scale & 3u))
+    return SAGE_ERR_ALIGN;
+  const size_t need = sage::qk_workspace(B, N, H, D, nr).bytes;
+  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
+  const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / q_block) * 4),
+                         range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / k_block) * 4),
+                         range_of(k_mean, bh * D * 2), range_of(workspace, need)};
+  const Range ins[2] = {range_of(q, view_bytes(B, N, H, D, q_sb, q_sn, q_sh)),
+                        range_of(k, view_bytes(B, N, H, D, k_sb, k_sn, k_sh))};
+  if (any_overlap(outs, 6, ins, 2)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,10 +119,16 @@ size_t sage_quant_qk_workspace_size(int B, int N, int H, int D) {
   return sage::qk_workspace(B, N, H, D).bytes;
 }
 
+size_t sage_norm_rope_quant_qk_workspace_size(int B, int N, int H, int D) {
+  if (check_shape(B, N, H, D) != SAGE_OK) return 0;
+  return sage::qk_workspace(B, N, H, D, true).bytes;
+}
+
 size_t sage_quant_v_workspace_size(int B, int N, int H, int D) {
   if (check_shape(B, N, H, D) != SAGE_OK) return 0;
   return sage::v_workspace(B, N, H, D).bytes;
 }
+
 
 int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                               const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
@@ -99,28 +136,8 @@ int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t
                               const int8_t* k_i8, const float* k_scale, const uint16_t* k_mean,
                               const void* workspace, size_t workspace_bytes, int q_block,
                               int k_block) {
-  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !workspace)
-    return SAGE_ERR_NULL;
-  int st = check_shape(B, N, H, D);
-  if (st != SAGE_OK) return st;
-  if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
-  if (k_block != SAGE_K_BLOCK && k_block != SAGE_K_FINE) return SAGE_ERR_UNSUPPORTED;
-  if ((st = check_strides(B, N, H, q_sb, q_sn, q_sh)) != SAGE_OK) return st;
-  if ((st = check_strides(B, N, H, k_sb, k_sn, k_sh)) != SAGE_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
-      !aligned16(k_mean) || !aligned16(workspace) || ((uintptr_t)q_scale & 3u) ||
-      ((uintptr_t)k_scale & 3u))
-    return SAGE_ERR_ALIGN;
-  const size_t need = sage::qk_workspace(B, N, H, D).bytes;
-  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
-  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
-  const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / q_block) * 4),
-                         range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / k_block) * 4),
-                         range_of(k_mean, bh * D * 2), range_of(workspace, need)};
-  const Range ins[2] = {range_of(q, view_bytes(B, N, H, D, q_sb, q_sn, q_sh)),
-                        range_of(k, view_bytes(B, N, H, D, k_sb, k_sn, k_sh))};
-  if (any_overlap(outs, 6, ins, 2)) return SAGE_ERR_OVERLAP;
-  return SAGE_OK;
+  return validate_qk(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8, q_scale, k_i8,
+                     k_scale, k_mean, workspace, workspace_bytes, q_block, k_block, false);
 }
 
 int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
@@ -197,7 +214,8 @@ int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, co
   if (st != SAGE_OK) return st;
   return status_of(sage::launch_quant_qk((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
                                          (const uint16_t*)k, B > 1 ? k_sb : 0, k_sn,
-                                         H > 1 ? k_sh : 0, B, N, H, D, q_block, k_block, q_i8, q_scale, k_i8,
+                                         H > 1 ? k_sh : 0, B, N, H, D, q_block, k_block, nullptr, q_i8,
+                                         q_scale, k_i8,
                                          k_scale, k_mean, workspace, (hipStream_t)stream));
 }
 
@@ -244,6 +262,79 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           out, o_sb, o_sn, o_sh, SAGE_Q_BLOCK, SAGE_K_BLOCK, stream);
 }
 
+int sage_validate_norm_rope(const void* x, int64_t x_sb, int64_t x_sn, int64_t x_sh, int B, int N,
+                            int H, int D, const uint16_t* w, const float* rope, float eps,
+                            const void* y, int64_t y_sb, int64_t y_sn, int64_t y_sh) {
+  if (!x || !w || !rope || !y) return SAGE_ERR_NULL;
+  int st = check_shape(B, N, H, D);
+  if (st != SAGE_OK) return st;
+  if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return SAGE_ERR_VALUE;
+  if ((st = check_strides(B, N, H, x_sb, x_sn, x_sh)) != SAGE_OK) return st;
+  if ((st = check_strides(B, N, H, y_sb, y_sn, y_sh)) != SAGE_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w) || !aligned16(rope)) return SAGE_ERR_ALIGN;
+  const Range outs[1] = {range_of(y, view_bytes(B, N, H, D, y_sb, y_sn, y_sh))};
+  const Range ins[3] = {range_of(x, view_bytes(B, N, H, D, x_sb, x_sn, x_sh)),
+                        range_of(w, (size_t)D * 2), range_of(rope, (size_t)N * D * 4)};
+  if (any_overlap(outs, 1, ins, 3)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_norm_rope(const void* x, int64_t x_sb, int64_t x_sn, int64_t x_sh, int B, int N, int H,
+                   int D, const uint16_t* w, const float* rope, float eps, void* y, int64_t y_sb,
+                   int64_t y_sn, int64_t y_sh, void* stream) {
+  const int st = sage_validate_norm_rope(x, x_sb, x_sn, x_sh, B, N, H, D, w, rope, eps, y, y_sb,
+                                         y_sn, y_sh);
+  if (st != SAGE_OK) return st;
+  return status_of(sage::launch_norm_rope((const uint16_t*)x, B > 1 ? x_sb : 0, N > 1 ? x_sn : 0,
+                                          H > 1 ? x_sh : 0, B, N, H, D, w, rope, (double)eps,
+                                          (uint16_t*)y, B > 1 ? y_sb : 0, N > 1 ? y_sn : 0,
+                                          H > 1 ? y_sh : 0, (hipStream_t)stream));
+}
+
+int sage_validate_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                                     const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                                     int B, int N, int H, int D, const uint16_t* wq,
+                                     const uint16_t* wk, const float* rope, float eps,
+                                     const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                     const float* k_scale, const uint16_t* k_mean,
+                                     const void* workspace, size_t workspace_bytes, int q_block,
+                                     int k_block) {
+  int st = validate_qk(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8, q_scale, k_i8,
+                       k_scale, k_mean, workspace, workspace_bytes, q_block, k_block, true);
+  if (st != SAGE_OK) return st;
+  if (!wq || !wk || !rope) return SAGE_ERR_NULL;
+  if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return SAGE_ERR_VALUE;
+  if (!aligned16(wq) || !aligned16(wk) || !aligned16(rope)) return SAGE_ERR_ALIGN;
+  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
+  const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / q_block) * 4),
+                         range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / k_block) * 4),
+                         range_of(k_mean, bh * D * 2),
+                         range_of(workspace, sage::qk_workspace(B, N, H, D, true).bytes)};
+  const Range ins[3] = {range_of(wq, (size_t)D * 2), range_of(wk, (size_t)D * 2),
+                        range_of(rope, (size_t)N * D * 4)};
+  if (any_overlap(outs, 6, ins, 3)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+                            int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
+                            const uint16_t* wq, const uint16_t* wk, const float* rope, float eps,
+                            int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                            uint16_t* k_mean, void* workspace, size_t workspace_bytes, int q_block,
+                            int k_block, void* stream) {
+  const int st = sage_validate_norm_rope_quant_qk(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N,
+                                                  H, D, wq, wk, rope, eps, q_i8, q_scale, k_i8,
+                                                  k_scale, k_mean, workspace, workspace_bytes,
+                                                  q_block, k_block);
+  if (st != SAGE_OK) return st;
+  const sage::NormRope nr{wq, wk, rope, (double)eps};
+  return status_of(sage::launch_quant_qk((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
+                                         (const uint16_t*)k, B > 1 ? k_sb : 0, k_sn,
+                                         H > 1 ? k_sh : 0, B, N, H, D, q_block, k_block, &nr, q_i8,
+                                         q_scale, k_i8, k_scale, k_mean, workspace,
+                                         (hipStream_t)stream));
+}
+
 int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
                            int* workgroups) {
   if (!waves_per_workgroup || !workgroups) return SAGE_ERR_NULL;
@@ -264,6 +355,7 @@ const char* sage_status_string(int status) {
     case SAGE_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case SAGE_ERR_OVERLAP: return "an output overlaps an input or another output";
     case SAGE_ERR_HIP: return "a HIP launch or runtime call failed";
+    case SAGE_ERR_VALUE: return "a scalar argument is out of range (eps must be finite and >= 0)";
     default: return "unknown status";
   }
 }

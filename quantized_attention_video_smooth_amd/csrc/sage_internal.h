@@ -27,16 +27,19 @@ inline StatsSplit stats_split(int B, int N, int H) {
   return StatsSplit{(int)ceil_div(N, rpc), rpc};
 }
 
-// sage_quant_qk workspace: fp64 partial sums [BH][nchunk][D].
+// sage_quant_qk workspace: fp64 partial sums [BH][nchunk][D]; with the QK
+// RMSNorm + RoPE producer in front (nr), also each K row's fp32 r [BH][Np],
+// written by the statistics pass and read by the quantisation pass.
 struct QkWorkspace {
-  size_t partial_off, bytes;
+  size_t partial_off, rk_off, bytes;
 };
-inline QkWorkspace qk_workspace(int B, int N, int H, int D) {
+inline QkWorkspace qk_workspace(int B, int N, int H, int D, bool nr = false) {
   StatsSplit s = stats_split(B, N, H);
   size_t bh = (size_t)B * H;
   QkWorkspace w;
   w.partial_off = 0;
-  w.bytes = align256(bh * s.nchunk * D * sizeof(double));
+  w.rk_off = align256(bh * s.nchunk * D * sizeof(double));
+  w.bytes = w.rk_off + (nr ? align256(bh * padded_tokens(N) * sizeof(float)) : 0);
   return w;
 }
 
@@ -57,12 +60,28 @@ inline VWorkspace v_workspace(int B, int N, int H, int D) {
   return w;
 }
 
+// The QK RMSNorm + RoPE producer's constants: bf16 weights [D] of the Q and
+// K norms, the (cos, sin) table fp32 [N][D/2][2], eps.
+struct NormRope {
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const float* rope;
+  double eps;
+};
+
+// nr == nullptr: Q and K are quantised as given; else they are the producer's
+// inputs and are normalised and rotated on the fly.
 hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                            const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
-                           int B, int N, int H, int D, int q_block, int k_block, int8_t* q_i8,
-                           float* q_scale,
+                           int B, int N, int H, int D, int q_block, int k_block, const NormRope* nr,
+                           int8_t* q_i8, float* q_scale,
                            int8_t* k_i8, float* k_scale, uint16_t* k_mean, void* workspace,
                            hipStream_t stream);
+
+hipError_t launch_norm_rope(const uint16_t* x, int64_t sb, int64_t sn, int64_t sh, int B, int N,
+                            int H, int D, const uint16_t* w, const float* rope, double eps,
+                            uint16_t* y, int64_t y_sb, int64_t y_sn, int64_t y_sh,
+                            hipStream_t stream);
 
 hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
                           int H, int D, uint8_t* v_fp8, float* v_scale, float* v_mean,

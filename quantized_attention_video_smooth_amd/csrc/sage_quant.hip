@@ -37,11 +37,15 @@ __device__ __forceinline__ int v_slot(int t) {
 // consecutive channels (one 16-byte load per token row); D/8 threads cover a
 // row, so a pass reads 256/(D/8) rows.
 // ---------------------------------------------------------------------------
-template <int D, bool IS_V>
+// NR: the rows are first put through the QK RMSNorm + RoPE producer
+// (weights nr_w, table rope), so the statistics are those of the producer's
+// output; each row's r is stored in rk [BH][Np] for the quantisation pass.
+template <int D, bool IS_V, bool NR = false>
 __global__ __launch_bounds__(kThreads) void stats_kernel(
     const uint16_t* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, int H, int N, int nchunk,
     int rows_per_chunk, double* __restrict__ psum, float* __restrict__ pmin,
-    float* __restrict__ pmax) {
+    float* __restrict__ pmax, const uint16_t* __restrict__ nr_w, const float* __restrict__ rope,
+    double eps, float* __restrict__ rk, int Np) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
   __shared__ double s_sum[RPP][D];
@@ -63,9 +67,24 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     mn[j] = __builtin_inff();
     mx[j] = -__builtin_inff();
   }
-  auto take = [&](const uint4& v) {
+  float w8[8];
+  if constexpr (NR) load_w8(nr_w, lc, w8);
+  // every lane of a token row takes the same path (the row index depends on
+  // the row, not the lane), as the producer's cross-lane sum needs
+  auto take = [&](const uint4& v, int row) {
     float f[8];
     unpack8(v, f);
+    if constexpr (NR) {
+      float f1[1][8], cs[1][8], r[1], r_own;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f1[0][j] = f[j];
+      load_cs8<D>(rope, row, lc, cs[0]);
+      rows_rsqrt<LPR, 1>(f1, eps, r, r_own);
+      if (lc == 0) rk[(size_t)bh * Np + row] = r_own;
+      norm_rope_apply<1>(f1, w8, cs, r);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = f1[0][j];
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       acc[j] += (double)f[j];
@@ -76,14 +95,39 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     }
   };
   int r = r0 + lr;
-  for (; r + 7 * RPP < r1; r += 8 * RPP) {  // 8 independent 16-byte loads in flight
-    uint4 v[8];
+  if constexpr (!NR) {
+    for (; r + 7 * RPP < r1; r += 8 * RPP) {  // 8 independent 16-byte loads in flight
+      uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *(const uint4*)(base + (int64_t)(r + u * RPP) * sn);
+      for (int u = 0; u < 8; ++u) v[u] = *(const uint4*)(base + (int64_t)(r + u * RPP) * sn);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) take(v[u]);
+      for (int u = 0; u < 8; ++u) take(v[u], r + u * RPP);
+    }
+  } else {
+    // 2 rows per step, data and table loads issued together, the producer
+    // run on both rows at once (2 rather than 4 rows: fewer live registers,
+    // more waves per SIMD to overlap the producer's arithmetic with loads)
+    for (; r + 1 * RPP < r1; r += 2 * RPP) {
+      uint4 v[2];
+      float f[2][8], cs[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        v[u] = *(const uint4*)(base + (int64_t)(r + u * RPP) * sn);
+        load_cs8<D>(rope, r + u * RPP, lc, cs[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) unpack8(v[u], f[u]);
+      float rr[2], r_own;
+      rows_rsqrt<LPR, 2>(f, eps, rr, r_own);
+      if ((lc & (LPR / 2 - 1)) == 0) rk[(size_t)bh * Np + r + (lc / (LPR / 2)) * RPP] = r_own;
+      norm_rope_apply<2>(f, w8, cs, rr);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += (double)f[u][j];
+    }
   }
-  for (; r < r1; r += RPP) take(*(const uint4*)(base + (int64_t)r * sn));
+  for (; r < r1; r += RPP) take(*(const uint4*)(base + (int64_t)r * sn), r);
 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -175,12 +219,16 @@ __global__ __launch_bounds__(D) void finalize_kernel(
 // blocks, or 64 per-token Q scales when q_block == 1).  Outputs are
 // head-major [B,H,Np,D].
 // ---------------------------------------------------------------------------
-template <int D>
+// NR: Q and K rows go through the QK RMSNorm + RoPE producer first (weights
+// wq / wk, table rope), as the statistics pass did for K.
+template <int D, bool NR = false>
 __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
     const uint16_t* __restrict__ q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
     const uint16_t* __restrict__ k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int H, int N, int Np,
     const uint16_t* __restrict__ k_mean, int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
-    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int q_block, int k_block) {
+    int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int q_block, int k_block,
+    const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
+    const float* __restrict__ rope, double eps, const float* __restrict__ rk) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
   constexpr int PASSES = 64 / RPP;
@@ -203,16 +251,40 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
     const uint4 m = *(const uint4*)(k_mean + (size_t)bh * D + lc * 8);
     unpack8(m, mean);
   }
+  float w8[8];
+  if constexpr (NR) load_w8(is_q ? wq : wk, lc, w8);
 
   float x[PASSES][8];
   float mp[PASSES];                // this thread's absmax in each pass
   float a_lo = 0.0f, a_hi = 0.0f;  // absmax of rows 0..31 and 32..63 of the tile
+  if constexpr (NR) {
+    // every lane loads (rows beyond N read row N-1 and are zeroed below), so
+    // the producer's cross-lane steps see whole groups; all loads first
+    uint4 raw[PASSES];
+    float cs[PASSES][8], rr[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = min(t * 64 + lr + p * RPP, N - 1);
+      raw[p] = *(const uint4*)(src + (int64_t)r * sn);
+      load_cs8<D>(rope, r, lc, cs[p]);
+      if (!is_q) rr[p] = rk[(size_t)bh * Np + r];  // K: r from the statistics pass
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) unpack8(raw[p], x[p]);
+    if (is_q) {
+      float r_own;
+      rows_rsqrt<LPR, PASSES>(x, eps, rr, r_own);
+    }
+    norm_rope_apply<PASSES>(x, w8, cs, rr);
+  }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = t * 64 + lr + p * RPP;
     if (r < N) {
-      const uint4 v = *(const uint4*)(src + (int64_t)r * sn);
-      unpack8(v, x[p]);
+      if constexpr (!NR) {
+        const uint4 v = *(const uint4*)(src + (int64_t)r * sn);
+        unpack8(v, x[p]);
+      }
       if (!is_q) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[p][j] = bf16_round_f32(x[p][j] - mean[j]);
@@ -420,19 +492,66 @@ __global__ __launch_bounds__(kThreads) void v_quant_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The QK RMSNorm + RoPE producer on its own, storing BF16 NHD (report card B):
+// grid (ceil(N*H / ROWS), B), 256 threads; a token row (n, h) per D/8 lanes,
+// 4 rows per thread, all loads issued before the arithmetic.
+// ---------------------------------------------------------------------------
 template <int D>
+__global__ __launch_bounds__(kThreads) void norm_rope_kernel(
+    const uint16_t* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, int N, int H,
+    const uint16_t* __restrict__ w, const float* __restrict__ rope, double eps,
+    uint16_t* __restrict__ y, int64_t y_sb, int64_t y_sn, int64_t y_sh) {
+  constexpr int LPR = D / 8;
+  constexpr int RPP = kThreads / LPR;
+  constexpr int PASSES = 4;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lr = tid / LPR, lc = tid - lr * LPR;
+  const int64_t rows = (int64_t)N * H;
+  float w8[8];
+  load_w8(w, lc, w8);
+  // every lane loads (rows beyond the last read the last row and are not
+  // stored), so the producer's cross-lane steps see whole groups
+  uint4 v[PASSES];
+  float f[PASSES][8], cs[PASSES][8];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t row = min((int64_t)blockIdx.x * (PASSES * RPP) + p * RPP + lr, rows - 1);
+    const int64_t n = row / H, h = row - n * H;
+    v[p] = *(const uint4*)(x + b * sb + n * sn + h * sh + 8 * lc);
+    load_cs8<D>(rope, n, lc, cs[p]);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) unpack8(v[p], f[p]);
+  norm_rope8_rows<LPR, PASSES>(f, w8, cs, eps);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t row = (int64_t)blockIdx.x * (PASSES * RPP) + p * RPP + lr;
+    if (row < rows) {
+      const int64_t n = row / H, h = row - n * H;
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = bf16x2_rne(f[p][2 * j], f[p][2 * j + 1]);  // exact: bf16 values
+      *(uint4*)(y + b * y_sb + n * y_sn + h * y_sh + 8 * lc) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+template <int D, bool NR>
 hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                          const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
-                         int H, int q_block, int k_block, int8_t* q_i8, float* q_scale,
-                         int8_t* k_i8, float* k_scale, uint16_t* k_mean, void* ws,
+                         int H, int q_block, int k_block, const NormRope& nr, int8_t* q_i8,
+                         float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean, void* ws,
                          hipStream_t stream) {
   const StatsSplit s = stats_split(B, N, H);
-  const QkWorkspace w = qk_workspace(B, N, H, D);
+  const QkWorkspace w = qk_workspace(B, N, H, D, NR);
   char* wsb = (char*)ws;
   const int Np = (int)padded_tokens(N);
-  hipLaunchKernelGGL((stats_kernel<D, false>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream, k,
-                     k_sb, k_sn, k_sh, H, N, s.nchunk, s.rows_per_chunk,
-                     (double*)(wsb + w.partial_off), (float*)nullptr, (float*)nullptr);
+  float* rk = NR ? (float*)(wsb + w.rk_off) : nullptr;
+  hipLaunchKernelGGL((stats_kernel<D, false, NR>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream,
+                     k, k_sb, k_sn, k_sh, H, N, s.nchunk, s.rows_per_chunk,
+                     (double*)(wsb + w.partial_off), (float*)nullptr, (float*)nullptr, nr.wk,
+                     nr.rope, nr.eps, rk, Np);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((finalize_kernel<D, false>), dim3(B * H), dim3(D), 0, stream,
@@ -440,9 +559,10 @@ hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t 
                      (const float*)nullptr, N, s.nchunk, k_mean, (float*)nullptr, (float*)nullptr,
                      (float*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((qk_quant_kernel<D>), dim3(Np / 64, B * H, 2), dim3(kThreads), 0, stream, q,
-                     q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, H, N, Np, (const uint16_t*)k_mean, q_i8,
-                     q_scale, k_i8, k_scale, q_block, k_block);
+  hipLaunchKernelGGL((qk_quant_kernel<D, NR>), dim3(Np / 64, B * H, 2), dim3(kThreads), 0, stream,
+                     q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, H, N, Np, (const uint16_t*)k_mean,
+                     q_i8, q_scale, k_i8, k_scale, q_block, k_block, nr.wq, nr.wk, nr.rope, nr.eps,
+                     (const float*)rk);
   return hipGetLastError();
 }
 
@@ -458,7 +578,8 @@ hipError_t quant_v_impl(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v
   hipLaunchKernelGGL((stats_kernel<D, true>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream, v,
                      v_sb, v_sn, v_sh, H, N, s.nchunk, s.rows_per_chunk,
                      (double*)(wsb + w.sum_off), (float*)(wsb + w.min_off),
-                     (float*)(wsb + w.max_off));
+                     (float*)(wsb + w.max_off), (const uint16_t*)nullptr, (const float*)nullptr, 0.0,
+                     (float*)nullptr, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((finalize_kernel<D, true>), dim3(B * H), dim3(D), 0, stream,
@@ -475,14 +596,35 @@ hipError_t quant_v_impl(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v
 
 hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                            const uint16_t* k, int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N,
-                           int H, int D, int q_block, int k_block, int8_t* q_i8, float* q_scale,
-                           int8_t* k_i8, float* k_scale, uint16_t* k_mean, void* workspace,
-                           hipStream_t stream) {
-  if (D == 128)
-    return quant_qk_impl<128>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, k_block,
-                              q_i8, q_scale, k_i8, k_scale, k_mean, workspace, stream);
-  return quant_qk_impl<64>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, k_block, q_i8,
-                           q_scale, k_i8, k_scale, k_mean, workspace, stream);
+                           int H, int D, int q_block, int k_block, const NormRope* nr, int8_t* q_i8,
+                           float* q_scale, int8_t* k_i8, float* k_scale, uint16_t* k_mean,
+                           void* workspace, hipStream_t stream) {
+  const NormRope none{nullptr, nullptr, nullptr, 0.0};
+#define SAGE_QK_IMPL(DD, NRR)                                                                    \
+  quant_qk_impl<DD, NRR>(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, q_block, k_block,     \
+                         nr ? *nr : none, q_i8, q_scale, k_i8, k_scale, k_mean, workspace, stream)
+  if (D == 128) return nr ? SAGE_QK_IMPL(128, true) : SAGE_QK_IMPL(128, false);
+  return nr ? SAGE_QK_IMPL(64, true) : SAGE_QK_IMPL(64, false);
+#undef SAGE_QK_IMPL
+}
+
+hipError_t launch_norm_rope(const uint16_t* x, int64_t sb, int64_t sn, int64_t sh, int B, int N,
+                            int H, int D, const uint16_t* w, const float* rope, double eps,
+                            uint16_t* y, int64_t y_sb, int64_t y_sn, int64_t y_sh,
+                            hipStream_t stream) {
+  const int64_t rows = (int64_t)N * H;
+  if (D == 128) {
+    constexpr int ROWS = 4 * (kThreads / 16);
+    hipLaunchKernelGGL((norm_rope_kernel<128>), dim3((unsigned)ceil_div(rows, ROWS), B),
+                       dim3(kThreads), 0, stream, x, sb, sn, sh, N, H, w, rope, eps, y, y_sb, y_sn,
+                       y_sh);
+  } else {
+    constexpr int ROWS = 4 * (kThreads / 8);
+    hipLaunchKernelGGL((norm_rope_kernel<64>), dim3((unsigned)ceil_div(rows, ROWS), B),
+                       dim3(kThreads), 0, stream, x, sb, sn, sh, N, H, w, rope, eps, y, y_sb, y_sn,
+                       y_sh);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,

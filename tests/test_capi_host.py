@@ -178,3 +178,87 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(s, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         s.lib()
+
+
+def test_norm_rope_validation(sage):
+    """sage_validate_norm_rope / sage_norm_rope: every refusal happens on the
+    host, before any HIP call."""
+    lib = sage.lib()
+    B, N, H, D = 2, 100, 3, 128
+    big = 1 << 40
+    x, w, rope, y = big, 2 * big, 3 * big, 4 * big
+    good = [x, N * H * D, H * D, D, B, N, H, D, w, rope, 1e-6, y, N * H * D, H * D, D]
+    assert lib.sage_validate_norm_rope(*good) == 0
+    for i, code in ((0, -1), (8, -1), (9, -1), (11, -1)):
+        bad = list(good)
+        bad[i] = None
+        assert lib.sage_validate_norm_rope(*bad) == code
+    for eps in (-1e-6, float("nan"), float("inf")):
+        bad = list(good)
+        bad[10] = eps
+        assert lib.sage_validate_norm_rope(*bad) == -9
+        assert lib.sage_norm_rope(*bad, None) == -9
+    bad = list(good)
+    bad[9] = rope + 8                        # the table is read 16 bytes at a time
+    assert lib.sage_validate_norm_rope(*bad) == -5
+    bad = list(good)
+    bad[8] = w + 2
+    assert lib.sage_validate_norm_rope(*bad) == -5
+    bad = list(good)
+    bad[11] = rope + N * D * 4 - 16          # y starts inside the table
+    assert lib.sage_validate_norm_rope(*bad) == -7
+    bad = list(good)
+    bad[11] = x + 64                         # y overlaps x
+    assert lib.sage_validate_norm_rope(*bad) == -7
+    bad = list(good)
+    bad[7] = 96
+    assert lib.sage_validate_norm_rope(*bad) == -3
+    assert lib.sage_status_string(-9) != lib.sage_status_string(-100)
+
+
+def test_norm_rope_quant_qk_validation(sage):
+    lib = sage.lib()
+    B, N, H, D = 1, 100, 2, 64
+    big = 1 << 40
+    qk = [big, 0, H * D, D, 2 * big, 0, H * D, D, B, N, H, D]
+    consts = [9 * big, 10 * big, 11 * big, 1e-6]
+    outs = [3 * big, 4 * big, 5 * big, 6 * big, 7 * big, 8 * big, 1 << 30]
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *consts, *outs, 32, 64) == 0
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *consts, *outs, 1, 16) == 0
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *consts, *outs, 2, 64) == -3
+    for i in range(3):
+        c = list(consts)
+        c[i] = None
+        assert lib.sage_validate_norm_rope_quant_qk(*qk, *c, *outs, 32, 64) == -1
+    c = list(consts)
+    c[3] = -1.0
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *c, *outs, 32, 64) == -9
+    assert lib.sage_norm_rope_quant_qk(*qk, *c, *outs, 32, 64, None) == -9
+    c = list(consts)
+    c[2] = 7 * big + 64                      # the table overlaps k_mean's range
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *c, *outs, 32, 64) == -7
+    c = list(consts)
+    c[0] = 9 * big + 4
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *c, *outs, 32, 64) == -5
+
+
+def test_norm_rope_quant_qk_workspace(sage):
+    """The fused producer's workspace is the quantiser's plus one fp32 per K
+    token row (rounded up to 256 bytes); a smaller one is refused."""
+    lib = sage.lib()
+    for B, N, H, D in ((1, 100, 2, 64), (2, 4608, 24, 128), (1, 32760, 40, 128)):
+        Np = sage.sage_padded_tokens(N)
+        base = lib.sage_quant_qk_workspace_size(B, N, H, D)
+        extra = (B * H * Np * 4 + 255) // 256 * 256
+        assert lib.sage_norm_rope_quant_qk_workspace_size(B, N, H, D) == base + extra
+    assert lib.sage_norm_rope_quant_qk_workspace_size(1, 100, 2, 96) == 0
+    B, N, H, D = 1, 100, 2, 64
+    big = 1 << 40
+    need = lib.sage_norm_rope_quant_qk_workspace_size(B, N, H, D)
+    qk = [big, 0, H * D, D, 2 * big, 0, H * D, D, B, N, H, D]
+    consts = [9 * big, 10 * big, 11 * big, 1e-6]
+    outs = [3 * big, 4 * big, 5 * big, 6 * big, 7 * big, 8 * big]
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *consts, *outs, need, 32, 64) == 0
+    assert lib.sage_validate_norm_rope_quant_qk(*qk, *consts, *outs, need - 1, 32, 64) == -6
+    assert lib.sage_validate_quant_qk_ex(*qk, *outs, lib.sage_quant_qk_workspace_size(B, N, H, D),
+                                         32, 64) == 0

@@ -70,6 +70,9 @@ def _load():
         "orc_attn_exact": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                             _i32, _i32, _i32, _i32, _dbl, _vp, _i32, _vp], None),
         "orc_norm_rope": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp], _i32),
+        "orc_quant_rows_e4m3": ([_vp, _i64, _i32, _i32, _vp, _vp], None),
+        "orc_gemm_fp8_rowwise": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
+                                  _vp, _vp], None),
         "orc_num_threads": ([], _i32),
     }
     for name, (args, res) in sig.items():
@@ -176,6 +179,45 @@ def norm_rope(x, weight, rope, eps: float = 1e-6):
     yb = y.view(torch.int16).numpy()
     bad = _load().orc_norm_rope(_p(xb), sb, sn, sh, B, N, H, D, _p(w), float(eps), _p(rope), _p(yb))
     return y, int(bad)
+
+
+def quant_rows_e4m3(x):
+    """Row-wise FP8 quantisation (orc_quant_rows_e4m3) of a bf16 torch CPU tensor
+    [M, K] (any row stride, unit column stride).  Returns (codes uint8 [M, K],
+    scales fp32 [M])."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    base = x.view(torch.int16).numpy()
+    codes = np.empty((M, K), np.uint8)
+    scales = np.empty(M, np.float32)
+    _load().orc_quant_rows_e4m3(_p(base), x.stride(0), M, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def gemm_fp8_rowwise(a, sa, b, sb, bias=None, rows=None, cols=None):
+    """Scaled FP8 GEMM (orc_gemm_fp8_rowwise) on codes a [M, K], b [N, K] with
+    row scales sa [M], sb [N] and optional bf16 torch bias [N].  Returns fp64
+    (out, absum) [len(rows), len(cols)]."""
+    import torch
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    rows = np.ascontiguousarray(np.arange(M) if rows is None else rows, dtype=np.int32)
+    cols = np.ascontiguousarray(np.arange(N) if cols is None else cols, dtype=np.int32)
+    bb = None
+    if bias is not None:
+        bb = np.ascontiguousarray(bias.contiguous().view(torch.int16).numpy())
+        assert bb.shape == (N,)
+    out = np.empty((rows.size, cols.size), np.float64)
+    absum = np.empty_like(out)
+    _load().orc_gemm_fp8_rowwise(_p(a), _p(sa), M, _p(b), _p(sb), N, K, _p(bb) if bb is not None else None,
+                                 _p(rows), rows.size, _p(cols), cols.size, _p(out), _p(absum))
+    return out, absum
 
 
 def k_mean(k):

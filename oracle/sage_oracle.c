@@ -416,6 +416,69 @@ int orc_quant_v(const uint16_t* v, int64_t sb, int64_t sn, int64_t sh, int B, in
 }
 
 /* ------------------------------------------------------------------------- */
+/* Row-wise FP8 projections                                                  */
+/* ------------------------------------------------------------------------- */
+
+/* Stage 02 of the report's §02 keeps the Q/K projections in BF16 and runs
+ * the other selected projections in row-wise FP8; the SGLang page's latency
+ * notes fix the form: E4M3 weights with one scale per output row, per-token
+ * activation scales, a scaled FP8 GEMM.  Reading: a row (a token of the
+ * activation, an output row of the weight) is quantised with the V rule:
+ * a = max_k |x[k]|, scale = a / 448, code = E4M3(fp32(x) * fp32(448 / a))
+ * (round to nearest even, saturating at +-448); a == 0 or 448/a not finite
+ * gives scale 0 and codes 0.  x is bf16 [M] rows of K values, row stride ld;
+ * codes [M][K], scales [M]. */
+void orc_quant_rows_e4m3(const uint16_t* x, int64_t ld, int M, int K, uint8_t* codes,
+                         float* scales) {
+#pragma omp parallel for schedule(static)
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* row = x + (int64_t)m * ld;
+    float a = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      float v = fabsf(orc_bf16_value(row[k]));
+      if (v > a) a = v;
+    }
+    const float inv = 448.0f / a;
+    const int zero = (a == 0.0f) || !isfinite(inv);
+    scales[m] = zero ? 0.0f : a / 448.0f;
+    for (int k = 0; k < K; ++k)
+      codes[(int64_t)m * K + k] = zero ? 0x00 : orc_e4m3_encode((double)(orc_bf16_value(row[k]) * inv));
+  }
+}
+
+/* The scaled FP8 GEMM on such codes, for the output entries (rows[i], cols[j]):
+ *   out = (sum_k dec(a[m][k]) dec(b[n][k])) * sa[m] * sb[n] + bias[n]
+ * in fp64 (bias bf16 [N], or NULL for none).  absum receives
+ *   sa[m] sb[n] sum_k |dec(a[m][k]) dec(b[n][k])| + |bias[n]|,
+ * the magnitude against which a GPU's fp32 accumulation error is bounded.
+ * a [M][K], b [N][K] (both K-contiguous); out, absum [nr][nc]. */
+void orc_gemm_fp8_rowwise(const uint8_t* a, const float* sa, int M, const uint8_t* b, const float* sb,
+                          int N, int K, const uint16_t* bias, const int32_t* rows, int nr,
+                          const int32_t* cols, int nc, double* out, double* absum) {
+  (void)M;
+  (void)N;
+  double lut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = orc_e4m3_decode((uint8_t)c);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int i = 0; i < nr; ++i)
+    for (int j = 0; j < nc; ++j) {
+      const int m = rows[i], n = cols[j];
+      const uint8_t* ar = a + (int64_t)m * K;
+      const uint8_t* br = b + (int64_t)n * K;
+      double acc = 0.0, aacc = 0.0;
+      for (int k = 0; k < K; ++k) {
+        const double t = lut[ar[k]] * lut[br[k]];
+        acc += t;
+        aacc += fabs(t);
+      }
+      const double s = (double)sa[m] * (double)sb[n];
+      const double bb = bias ? (double)orc_bf16_value(bias[n]) : 0.0;
+      out[(int64_t)i * nc + j] = acc * s + bb;
+      absum[(int64_t)i * nc + j] = aacc * s + fabs(bb);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Attention                                                                 */
 /* ------------------------------------------------------------------------- */
 

@@ -25,6 +25,10 @@ the pre-norm Q and K are the tensors above; `norm_weight` draws the per-channel
 weights 1 + 0.1 z (bf16); `rope_table` builds the cos / sin of each token's
 rotation angles from a synthetic 4-axis position grid (the pages give neither
 the axis sizes nor the frequencies; see the function).
+
+Inputs of the row-wise FP8 projection (report §02 stage 02; SGLang page latency
+notes): `proj_inputs` draws the activation X ~ N(0, 1), the weight
+W ~ N(0, 1/K) and the bias ~ N(0, 0.01), all bf16.
 """
 from __future__ import annotations
 
@@ -45,6 +49,7 @@ STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
 STREAM_K_OFF, STREAM_V_OFF, STREAM_Q_OFF = 4, 5, 6
 STREAM_OUTLIER = 7
 STREAM_QW, STREAM_KW = 8, 9
+STREAM_PX, STREAM_PW, STREAM_PB = 10, 11, 12
 
 
 def build() -> str:
@@ -246,3 +251,20 @@ def rope_table(N: int, D: int, theta: float = 10000.0) -> np.ndarray:
     out[..., 0] = np.cos(ang)
     out[..., 1] = np.sin(ang)
     return out
+
+
+PROJ_SHAPES = {
+    # the V + MLP projection of a FLUX.3-Action-like joint block: tokens
+    # B*N = 2*4608, hidden H*D = 24*128, outputs V (hidden) + MLP (4 hidden)
+    "vmlp_proj": (2 * 4608, 3072, 3072 + 4 * 3072),
+}
+
+
+def proj_inputs(M: int, K: int, N: int, seed: int = 0, tag: int = 200):
+    """(x [M, K], w [N, K], bias [N]) bf16 torch tensors; `tag` keys the streams."""
+    import torch
+    x = normals(seed, tag, STREAM_PX, M * K).reshape(M, K)
+    w = normals(seed, tag, STREAM_PW, N * K).reshape(N, K) / math.sqrt(K)
+    b = normals(seed, tag, STREAM_PB, N) * 0.1
+    cast = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    return cast(x), cast(w), cast(b)

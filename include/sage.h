@@ -13,7 +13,11 @@
  *   "MiniMax H3 on DGX Spark", §01 precision map (QK INT8 / PV FP8).
  *   "Why can an A10 run FLUX.1", §1.1 (E4M3: 4 exponent, 3 mantissa bits).
  *   "FLUX 3 Action" SGLang page: §1 (4-axis (t, h, w, l) RoPE in the joint
- *     blocks) and the latency notes (QK RMSNorm + RoPE as one fused kernel).
+ *     blocks) and the latency notes (QK RMSNorm + RoPE as one fused kernel;
+ *     row-wise FP8 projections: E4M3 weights, one scale per output row,
+ *     per-token activation scales, a scaled FP8 GEMM).
+ *   "FLUX.3 Action RTX 5090 report", §02 stage 02 (mixed-precision
+ *     projections: Q/K projections BF16, other selected projections row-wise FP8).
  *
  * Conventions shared by every entry point
  *   - Tensors named "[B,N,H,D]" are bf16 (uint16 bit patterns) in token-major
@@ -263,6 +267,39 @@ int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
                      void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block,
                      void* stream);
 
+/*
+ * sage_quant_rows_fp8 -- row-wise E4M3 quantisation of a bf16 matrix (report
+ * §02 stage 02; SGLang page: per-token activation scales, one scale per
+ * weight output row).  For each row m of x (K values):
+ *   a = max_k |x[m,k]|,  scales[m] = a / 448,
+ *   codes[m,k] = E4M3FN( fp32(x[m,k]) * fp32(448 / a) )   RNE, saturating;
+ * a == 0 (or 448 / a overflowing) gives scale 0 and codes 0x00.  The rule is
+ * that of sage_quant_v.
+ * Input (device): x bf16 [M, ldx] row-major (ldx >= K, multiple of 8),
+ * 16-byte aligned.  Outputs (device): codes uint8 [M, K] contiguous (16-byte
+ * aligned), scales fp32 [M].  Supported: 1 <= M, 8 <= K <= 16384, K % 8 == 0.
+ */
+int sage_quant_rows_fp8(const void* x, int64_t ldx, int M, int K, uint8_t* codes, float* scales,
+                        void* stream);
+
+/*
+ * sage_gemm_fp8_rowwise -- the scaled FP8 GEMM of a row-wise FP8 projection:
+ *   out[m,n] = bf16( (sum_k x8[m,k] w8[n,k]) * x_scale[m] * w_scale[n] + bias[n] )
+ * with E4M3 codes from sage_quant_rows_fp8, the sum accumulated in fp32 on the
+ * matrix cores, the scales applied in fp32 in that order, bias bf16 [N] (or
+ * NULL), RNE to bf16.  out may be a column slice of a wider buffer (e.g. the
+ * V + MLP projection whose V part sage_quant_v then reads in place).
+ * Inputs (device): x8 uint8 [M, K], w8 uint8 [N, K] (row-major, 16-byte
+ * aligned), x_scale fp32 [M], w_scale fp32 [N] (16-byte aligned), bias
+ * (8-byte aligned).  Output (device): out bf16 [M, ldo] row-major, ldo >= N,
+ * ldo % 4 == 0, 8-byte aligned; it must not overlap an input.
+ * Supported: M >= 1, N >= 4 with N % 4 == 0, K >= 128 with K % 128 == 0,
+ * M, N <= 2^24 (else SAGE_ERR_UNSUPPORTED / SAGE_ERR_SHAPE).
+ */
+int sage_gemm_fp8_rowwise(const uint8_t* x8, const float* x_scale, int M, const uint8_t* w8,
+                          const float* w_scale, int N, int K, const void* bias, void* out,
+                          int64_t ldo, void* stream);
+
 /* Launch shape that sage_attn_fwd uses for these sizes on the current device:
  * waves per workgroup (32 queries each) and workgroups launched.  Eight waves
  * (256 queries per workgroup, one per CU) when the grid is at least eight such
@@ -316,6 +353,12 @@ int sage_validate_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, 
                                      const int8_t* k_i8, const float* k_scale,
                                      const uint16_t* k_mean, const void* workspace,
                                      size_t workspace_bytes, int q_block, int k_block);
+
+int sage_validate_quant_rows_fp8(const void* x, int64_t ldx, int M, int K, const uint8_t* codes,
+                                 const float* scales);
+int sage_validate_gemm_fp8_rowwise(const uint8_t* x8, const float* x_scale, int M,
+                                   const uint8_t* w8, const float* w_scale, int N, int K,
+                                   const void* bias, const void* out, int64_t ldo);
 
 /* Static, never-NULL description of a status code. */
 const char* sage_status_string(int status);

@@ -72,7 +72,7 @@ def _load():
         "orc_norm_rope": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp], _i32),
         "orc_quant_rows_e4m3": ([_vp, _i64, _i32, _i32, _vp, _vp], None),
         "orc_gemm_fp8_rowwise": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
-                                  _vp, _vp], None),
+                                  _vp, _vp, _vp], None),
         "orc_num_threads": ([], _i32),
     }
     for name, (args, res) in sig.items():
@@ -198,7 +198,8 @@ def quant_rows_e4m3(x):
 def gemm_fp8_rowwise(a, sa, b, sb, bias=None, rows=None, cols=None):
     """Scaled FP8 GEMM (orc_gemm_fp8_rowwise) on codes a [M, K], b [N, K] with
     row scales sa [M], sb [N] and optional bf16 torch bias [N].  Returns fp64
-    (out, absum) [len(rows), len(cols)]."""
+    (out, absum, blk) [len(rows), len(cols)]: the result and the two error
+    magnitudes described in orc_gemm_fp8_rowwise."""
     import torch
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
@@ -215,9 +216,10 @@ def gemm_fp8_rowwise(a, sa, b, sb, bias=None, rows=None, cols=None):
         assert bb.shape == (N,)
     out = np.empty((rows.size, cols.size), np.float64)
     absum = np.empty_like(out)
+    blk = np.empty_like(out)
     _load().orc_gemm_fp8_rowwise(_p(a), _p(sa), M, _p(b), _p(sb), N, K, _p(bb) if bb is not None else None,
-                                 _p(rows), rows.size, _p(cols), cols.size, _p(out), _p(absum))
-    return out, absum
+                                 _p(rows), rows.size, _p(cols), cols.size, _p(out), _p(absum), _p(blk))
+    return out, absum, blk
 
 
 def k_mean(k):

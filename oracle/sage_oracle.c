@@ -448,13 +448,17 @@ void orc_quant_rows_e4m3(const uint16_t* x, int64_t ld, int M, int K, uint8_t* c
 
 /* The scaled FP8 GEMM on such codes, for the output entries (rows[i], cols[j]):
  *   out = (sum_k dec(a[m][k]) dec(b[n][k])) * sa[m] * sb[n] + bias[n]
- * in fp64 (bias bf16 [N], or NULL for none).  absum receives
- *   sa[m] sb[n] sum_k |dec(a[m][k]) dec(b[n][k])| + |bias[n]|,
- * the magnitude against which a GPU's fp32 accumulation error is bounded.
- * a [M][K], b [N][K] (both K-contiguous); out, absum [nr][nc]. */
+ * in fp64 (bias bf16 [N], or NULL for none).  Two magnitudes for the tests'
+ * error bounds (not part of the result):
+ *   absum = sa[m] sb[n] sum_k |p_k| + |bias[n]|,  p_k = dec(a[m][k]) dec(b[n][k]);
+ *   blk   = sa[m] sb[n] sum over 64-term blocks of k (ascending) of
+ *           (|exact sum of the earlier blocks| + max |p_k| in the block),
+ * the magnitude that bounds a blocked accumulator which adds 64 products at a
+ * time to its running value with a fixed number of bits below the larger of
+ * the two.  a [M][K], b [N][K] (both K-contiguous); out, absum, blk [nr][nc]. */
 void orc_gemm_fp8_rowwise(const uint8_t* a, const float* sa, int M, const uint8_t* b, const float* sb,
                           int N, int K, const uint16_t* bias, const int32_t* rows, int nr,
-                          const int32_t* cols, int nc, double* out, double* absum) {
+                          const int32_t* cols, int nc, double* out, double* absum, double* blk) {
   (void)M;
   (void)N;
   double lut[256];
@@ -465,16 +469,23 @@ void orc_gemm_fp8_rowwise(const uint8_t* a, const float* sa, int M, const uint8_
       const int m = rows[i], n = cols[j];
       const uint8_t* ar = a + (int64_t)m * K;
       const uint8_t* br = b + (int64_t)n * K;
-      double acc = 0.0, aacc = 0.0;
+      double acc = 0.0, aacc = 0.0, bacc = 0.0, bmax = 0.0, before = 0.0;
       for (int k = 0; k < K; ++k) {
+        if (k % 64 == 0) before = fabs(acc);
         const double t = lut[ar[k]] * lut[br[k]];
         acc += t;
         aacc += fabs(t);
+        if (fabs(t) > bmax) bmax = fabs(t);
+        if (k % 64 == 63 || k == K - 1) {
+          bacc += before + bmax;
+          bmax = 0.0;
+        }
       }
       const double s = (double)sa[m] * (double)sb[n];
       const double bb = bias ? (double)orc_bf16_value(bias[n]) : 0.0;
       out[(int64_t)i * nc + j] = acc * s + bb;
       absum[(int64_t)i * nc + j] = aacc * s + fabs(bb);
+      blk[(int64_t)i * nc + j] = bacc * s;
     }
 }
 

@@ -69,6 +69,10 @@ _SIGS = {
     "sage_validate_norm_rope_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32,
                                           _i32, _i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
                                           _vp, _vp, _vp, _sz, _i32, _i32], _i32),
+    "sage_quant_rows_fp8": ([_vp, _i64, _i32, _i32, _vp, _vp, _vp], _i32),
+    "sage_validate_quant_rows_fp8": ([_vp, _i64, _i32, _i32, _vp, _vp], _i32),
+    "sage_gemm_fp8_rowwise": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
+    "sage_validate_gemm_fp8_rowwise": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i64], _i32),
     "sage_validate_attn_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                    _vp, _i64, _i64, _i64, _i32, _i32], _i32),
     "sage_status_string": ([_i32], ctypes.c_char_p),
@@ -123,6 +127,14 @@ def sage_quant_qk_ex(*args) -> int:
 
 def sage_attn_fwd_ex(*args) -> int:
     return lib().sage_attn_fwd_ex(*args)
+
+
+def sage_quant_rows_fp8(*args) -> int:
+    return lib().sage_quant_rows_fp8(*args)
+
+
+def sage_gemm_fp8_rowwise(*args) -> int:
+    return lib().sage_gemm_fp8_rowwise(*args)
 
 
 def sage_norm_rope(*args) -> int:
@@ -244,6 +256,41 @@ def norm_rope_quant_qk(q, k, wq, wk, rope, eps: float = 1e-6, stream=None, q_blo
                                    q_block, k_block, _stream_ptr(stream)),
            "sage_norm_rope_quant_qk")
     return q_i8, q_scale, k_i8, k_scale, k_mean
+
+
+def quant_rows_fp8(x, stream=None):
+    """Row-wise E4M3 quantisation: x bf16 [M, K] (row stride any multiple of 8, unit
+    column stride) -> (codes uint8 [M, K], scales fp32 [M])."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a CUDA bf16 [M, K] tensor with unit column stride")
+    M, K = x.shape
+    codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(sage_quant_rows_fp8(x.data_ptr(), x.stride(0), M, K, codes.data_ptr(), scales.data_ptr(),
+                               _stream_ptr(stream)), "sage_quant_rows_fp8")
+    return codes, scales
+
+
+def gemm_fp8_rowwise(x8, x_scale, w8, w_scale, bias=None, out=None, stream=None):
+    """Scaled FP8 GEMM: codes x8 [M, K], w8 [N, K] with row scales -> bf16 [M, N]
+    (or fills `out`, which may be a column slice of a wider [M, *] buffer)."""
+    import torch
+    M, K = x8.shape
+    N = w8.shape[0]
+    for t, name in ((x8, "x8"), (w8, "w8")):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous CUDA uint8 tensor")
+    if w8.shape[1] != K:
+        raise ValueError("x8 and w8 must have the same K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x8.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a bf16 [M, N] view with unit column stride")
+    _check(sage_gemm_fp8_rowwise(x8.data_ptr(), x_scale.data_ptr(), M, w8.data_ptr(), w_scale.data_ptr(),
+                                 N, K, bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                                 out.stride(0), _stream_ptr(stream)), "sage_gemm_fp8_rowwise")
+    return out
 
 
 def quant_qk(q, k, stream=None, q_block: int = 32, k_block: int = 64):

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsage.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["sage_capi.hip", "sage_quant.hip", "sage_attn.hip"]
+SOURCES = ["sage_capi.hip", "sage_quant.hip", "sage_attn.hip", "sage_proj.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -335,6 +335,56 @@ int sage_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q
                                          (hipStream_t)stream));
 }
 
+int sage_validate_quant_rows_fp8(const void* x, int64_t ldx, int M, int K, const uint8_t* codes,
+                                 const float* scales) {
+  if (!x || !codes || !scales) return SAGE_ERR_NULL;
+  if (M < 1 || K < 8 || (int64_t)M * K >= ((int64_t)1 << 40)) return SAGE_ERR_SHAPE;
+  if (K % 8 != 0 || K > 16384) return SAGE_ERR_UNSUPPORTED;
+  if (ldx < K) return SAGE_ERR_STRIDE;
+  if (ldx % 8 != 0 || !aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 3u))
+    return SAGE_ERR_ALIGN;
+  const Range outs[2] = {range_of(codes, (size_t)M * K), range_of(scales, (size_t)M * 4)};
+  const Range ins[1] = {range_of(x, ((size_t)(M - 1) * ldx + K) * 2)};
+  if (any_overlap(outs, 2, ins, 1)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_quant_rows_fp8(const void* x, int64_t ldx, int M, int K, uint8_t* codes, float* scales,
+                        void* stream) {
+  const int st = sage_validate_quant_rows_fp8(x, ldx, M, K, codes, scales);
+  if (st != SAGE_OK) return st;
+  return status_of(sage::launch_quant_rows_fp8((const uint16_t*)x, ldx, M, K, codes, scales,
+                                               (hipStream_t)stream));
+}
+
+int sage_validate_gemm_fp8_rowwise(const uint8_t* x8, const float* x_scale, int M,
+                                   const uint8_t* w8, const float* w_scale, int N, int K,
+                                   const void* bias, const void* out, int64_t ldo) {
+  if (!x8 || !x_scale || !w8 || !w_scale || !out) return SAGE_ERR_NULL;
+  if (M < 1 || N < 1 || K < 1 || M > (1 << 24) || N > (1 << 24)) return SAGE_ERR_SHAPE;
+  if (K % 128 != 0 || N % 4 != 0) return SAGE_ERR_UNSUPPORTED;
+  if (ldo < N) return SAGE_ERR_STRIDE;
+  if (ldo % 4 != 0 || !aligned16(x8) || !aligned16(w8) || !aligned16(w_scale) ||
+      ((uintptr_t)x_scale & 3u) || ((uintptr_t)bias & 7u) || ((uintptr_t)out & 7u))
+    return SAGE_ERR_ALIGN;
+  const Range outs[1] = {range_of(out, ((size_t)(M - 1) * ldo + N) * 2)};
+  const Range ins[5] = {range_of(x8, (size_t)M * K), range_of(x_scale, (size_t)M * 4),
+                        range_of(w8, (size_t)N * K), range_of(w_scale, (size_t)N * 4),
+                        range_of(bias, bias ? (size_t)N * 2 : 0)};
+  if (any_overlap(outs, 1, ins, 5)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_gemm_fp8_rowwise(const uint8_t* x8, const float* x_scale, int M, const uint8_t* w8,
+                          const float* w_scale, int N, int K, const void* bias, void* out,
+                          int64_t ldo, void* stream) {
+  const int st = sage_validate_gemm_fp8_rowwise(x8, x_scale, M, w8, w_scale, N, K, bias, out, ldo);
+  if (st != SAGE_OK) return st;
+  return status_of(sage::launch_gemm_fp8_rowwise(x8, x_scale, M, w8, w_scale, N, K,
+                                                 (const uint16_t*)bias, (uint16_t*)out, ldo,
+                                                 (hipStream_t)stream));
+}
+
 int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
                            int* workgroups) {
   if (!waves_per_workgroup || !workgroups) return SAGE_ERR_NULL;

@@ -96,4 +96,12 @@ hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_
                            int k_block, float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
                            hipStream_t stream);
 
+// Row-wise FP8 projections.
+hipError_t launch_quant_rows_fp8(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* codes,
+                                 float* scales, hipStream_t stream);
+void gemm_fp8_shape(int M, int N, int* workgroups);
+hipError_t launch_gemm_fp8_rowwise(const uint8_t* x8, const float* sx, int M, const uint8_t* w8,
+                                   const float* sw, int N, int K, const uint16_t* bias,
+                                   uint16_t* out, int64_t ldo, hipStream_t stream);
+
 }  // namespace sage

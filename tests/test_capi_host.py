@@ -262,3 +262,43 @@ def test_norm_rope_quant_qk_workspace(sage):
     assert lib.sage_validate_norm_rope_quant_qk(*qk, *consts, *outs, need - 1, 32, 64) == -6
     assert lib.sage_validate_quant_qk_ex(*qk, *outs, lib.sage_quant_qk_workspace_size(B, N, H, D),
                                          32, 64) == 0
+
+
+def test_projection_validation(sage):
+    """sage_validate_quant_rows_fp8 / sage_validate_gemm_fp8_rowwise refuse bad
+    arguments on the host, with the same codes the entry points return."""
+    lib = sage.lib()
+    big = 1 << 40
+    M, K, N = 300, 3072, 512
+    assert lib.sage_validate_quant_rows_fp8(big, K, M, K, 2 * big, 3 * big) == 0
+    assert lib.sage_validate_quant_rows_fp8(big, K + 64, M, K, 2 * big, 3 * big) == 0
+    assert lib.sage_validate_quant_rows_fp8(None, K, M, K, 2 * big, 3 * big) == -1
+    assert lib.sage_validate_quant_rows_fp8(big, K, 0, K, 2 * big, 3 * big) == -2
+    assert lib.sage_validate_quant_rows_fp8(big, K, M, 12, 2 * big, 3 * big) == -3
+    assert lib.sage_validate_quant_rows_fp8(big, 32768, M, 32768, 2 * big, 3 * big) == -3
+    assert lib.sage_validate_quant_rows_fp8(big, K - 8, M, K, 2 * big, 3 * big) == -4
+    assert lib.sage_validate_quant_rows_fp8(big, K + 4, M, K, 2 * big, 3 * big) == -5
+    assert lib.sage_validate_quant_rows_fp8(big + 8, K, M, K, 2 * big, 3 * big) == -5
+    assert lib.sage_validate_quant_rows_fp8(big, K, M, K, big + 64, 3 * big) == -7
+    assert lib.sage_quant_rows_fp8(big, K, M, 12, 2 * big, 3 * big, None) == -3
+    g = [big, 2 * big, M, 3 * big, 4 * big, N, K, 5 * big, 6 * big, N]
+    assert lib.sage_validate_gemm_fp8_rowwise(*g) == 0
+    bad = list(g); bad[7] = None
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == 0          # no bias
+    bad = list(g); bad[3] = None
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -1
+    bad = list(g); bad[6] = 3000
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -3         # K % 128
+    bad = list(g); bad[5] = 510; bad[9] = 512
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -3         # N % 4
+    bad = list(g); bad[9] = N - 4
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -4         # ldo < N
+    bad = list(g); bad[9] = N + 2
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -5
+    bad = list(g); bad[4] = 4 * big + 4                           # w_scale read as float4
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -5
+    bad = list(g); bad[8] = 3 * big + 1024                        # out inside w8
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -7
+    assert lib.sage_gemm_fp8_rowwise(*bad, None) == -7
+    bad = list(g); bad[2] = (1 << 24) + 1
+    assert lib.sage_validate_gemm_fp8_rowwise(*bad) == -2

@@ -83,14 +83,21 @@ def test_gemm_matches_numpy_matmul(xw):
     x, w, b = xw
     ca, sa = oracle.quant_rows_e4m3(x)
     cb, sb = oracle.quant_rows_e4m3(w)
-    out, absum = oracle.gemm_fp8_rowwise(ca, sa, cb, sb, bias=b)
+    out, absum, blk = oracle.gemm_fp8_rowwise(ca, sa, cb, sb, bias=b)
     A, Bm = oracle.e4m3_decode(ca), oracle.e4m3_decode(cb)
     want = (A @ Bm.T) * sa.astype(np.float64)[:, None] * sb.astype(np.float64)[None, :] + b.double().numpy()[None, :]
     np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-12)
     wabs = (np.abs(A) @ np.abs(Bm).T) * sa[:, None] * sb[None, :] + np.abs(b.double().numpy())[None, :]
     np.testing.assert_allclose(absum, wabs, rtol=1e-12, atol=1e-12)
+    # blk: sum over 64-blocks of |earlier partial sum| + the block's largest |product|
+    P = A[:, None, :] * Bm[None, :, :]                               # [M, N, K]
+    K = A.shape[1]
+    pre = np.concatenate([np.zeros(P.shape[:2] + (1,)), np.cumsum(P, -1)[..., 63:K - 1:64]], -1)
+    bmax = np.abs(P).reshape(P.shape[0], P.shape[1], -1, 64).max(-1)
+    wblk = (np.abs(pre) + bmax).sum(-1) * sa[:, None] * sb[None, :]
+    np.testing.assert_allclose(blk, wblk, rtol=1e-9, atol=1e-12)
     rows, cols = np.array([0, 5, 36], np.int32), np.array([28, 3], np.int32)
-    sub, _ = oracle.gemm_fp8_rowwise(ca, sa, cb, sb, bias=b, rows=rows, cols=cols)
+    sub, _, _ = oracle.gemm_fp8_rowwise(ca, sa, cb, sb, bias=b, rows=rows, cols=cols)
     np.testing.assert_array_equal(sub, out[np.ix_(rows, cols)])
 
 
@@ -103,5 +110,5 @@ def test_gemm_identity_weight_returns_the_dequantised_rows(xw):
     cb = np.zeros((K, K), np.uint8)
     np.fill_diagonal(cb, 0x38)
     assert oracle.e4m3_decode(np.array([0x38], np.uint8))[0] == 1.0
-    out, _ = oracle.gemm_fp8_rowwise(ca, sa, cb, np.ones(K, np.float32))
+    out, _, _ = oracle.gemm_fp8_rowwise(ca, sa, cb, np.ones(K, np.float32))
     np.testing.assert_array_equal(out, oracle.e4m3_decode(ca) * sa.astype(np.float64)[:, None])

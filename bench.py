@@ -94,6 +94,17 @@ def cpu_baseline(workload_cfg, seed=0):
     }
 
 
+def copy_calibration(torch, dev):
+    """One 256 MiB device-to-device copy: a kernel of known HBM traffic for
+    scaling FETCH_SIZE / WRITE_SIZE counter readings."""
+    src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def proj_cpu_baseline(M, K, N, seed=0):
     """The oracle on a bounded sample of the projection: the row quantisation of
     X and W in full, the scaled GEMM on every 8th output row and column,
@@ -243,7 +254,10 @@ def main():
         sys.exit(1)
     lib = sage.lib()
     if args.workload == "vmlp_proj":
-        print(json.dumps(run_projection(args, torch, synth, sage)), flush=True)
+        res = run_projection(args, torch, synth, sage)
+        if args.copy_calibration:
+            copy_calibration(torch, torch.device("cuda:0"))
+        print(json.dumps(res), flush=True)
         return
     cfg = synth.config(args.workload)
     B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
@@ -429,12 +443,7 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
     if args.copy_calibration:
-        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, dev)
     print(json.dumps(res), flush=True)
 
 

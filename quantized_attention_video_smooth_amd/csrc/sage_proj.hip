@@ -14,9 +14,10 @@
 // so a lane's accumulators hold 4 consecutive outputs n of one token m per
 // register group (8-byte bf16 stores in the epilogue).  A workgroup of 8
 // waves computes a 256 (n) x 256 (m) block; each wave a 128 x 64 part of it
-// (8 accumulator tiles).  K advances in 128-byte steps through a two-stage LDS
-// ring filled by direct global->LDS loads, with the 16-byte chunks of each row
-// XOR-swizzled so the operand reads are free of bank conflicts.
+// (8 accumulator tiles).  K advances in 64-byte steps through a four-slot LDS
+// ring, three stages ahead, filled by direct global->LDS loads, with the
+// 16-byte chunks of each row XOR-swizzled so the operand reads are free of
+// bank conflicts.
 #include <hip/hip_runtime.h>
 
 #include "sage_device.h"
@@ -86,7 +87,8 @@ struct GemmCfg {
   static constexpr int NT = NW * 64;     // threads
   static constexpr int BN = 256;         // output rows n per workgroup (W rows)
   static constexpr int BM = 256;         // tokens m per workgroup (X rows)
-  static constexpr int BK = 128;         // bytes of K per stage
+  static constexpr int BK = 64;          // bytes of K per stage (one MFMA k-step)
+  static constexpr int NBUF = 4;         // LDS ring depth (= stages in flight, see the loop)
   static constexpr int JN = BK / 16;     // 16-byte chunks per tile row
   static constexpr int ACH = BN * JN;    // chunks of the W tile
   static constexpr int BCH = BM * JN;    // chunks of the X tile
@@ -97,10 +99,12 @@ struct GemmCfg {
   static_assert(CPT * NT == ACH + BCH && ACH % NT == 0, "stage copy must split evenly");
 };
 
-// LDS chunk position of row r, chunk j: rows of JN = 8 chunks (128 bytes),
+// LDS chunk position of row r, chunk j: rows of JN = 4 chunks (64 bytes),
 // chunk index XOR-swizzled by the row so that the 16 lanes of a ds_read_b128
-// pass (16 consecutive rows, one logical chunk) hit 16 distinct bank groups.
-__device__ __forceinline__ int gk_pos(int r, int j) { return 8 * r + (j ^ ((r >> 1) & 7)); }
+// pass (16 consecutive rows, one logical chunk) hit 16 distinct 16-byte bank
+// groups of the 256-byte bank row: 4 (r % 4) + (j ^ ((r / 4) % 4)) is
+// distinct over any 16 consecutive rows.
+__device__ __forceinline__ int gk_pos(int r, int j) { return 4 * r + (j ^ ((r >> 2) & 3)); }
 
 __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
     const uint8_t* __restrict__ x8, const float* __restrict__ sx, int M,
@@ -108,15 +112,24 @@ __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int64_t ldo, int n_mblk,
     int total) {
   using C = GemmCfg;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NBUF * C::STAGE];
 
-  // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a
-  // contiguous run of output blocks, m fastest, so the W block of a run stays
-  // in that XCD's L2 while the X blocks stream past it.
+  // XCD-aware, grouped order.  Workgroup i runs on XCD i % 8: each XCD gets a
+  // contiguous run of logical blocks, and within it the ~32 workgroups that run
+  // at once (one per CU) form GN n-blocks x 32/GN m-blocks, walking through K
+  // roughly together: each K slice they need comes from GN W blocks and 32/GN
+  // X blocks (12 for GN = 8) rather than from 1 W and 32 X blocks, so most
+  // requests hit the XCD's L2 instead of going to the memory-side cache.
+  constexpr int GN = 8;
   const int per_xcd = gridDim.x / 8;
   const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (logical >= total) return;  // whole workgroup, before any barrier
-  const int nb = logical / n_mblk, mb = logical - nb * n_mblk;
+  const int n_nblk = total / n_mblk;
+  const int grp = logical / (GN * n_mblk);
+  const int first_nb = grp * GN;
+  const int gsize = min(n_nblk - first_nb, GN);
+  const int in_grp = logical - grp * GN * n_mblk;
+  const int nb = first_nb + in_grp % gsize, mb = in_grp / gsize;
   const int n_base = nb * C::BN, m_base = mb * C::BM;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -136,13 +149,13 @@ __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
     const bool xb = g >= C::ACH;
     const int gg = xb ? g - C::ACH : g;
     const int r = gg / C::JN, jx = gg % C::JN;
-    const int j = jx ^ ((r >> 1) & 7);
+    const int j = jx ^ ((r >> 2) & 3);
     if (!xb) goff[i] = (int64_t)min(n_base + r, N - 1) * K + 16 * j;
     else goff[i] = (int64_t)min(m_base + r, M - 1) * K + 16 * j;
     is_x[i] = xb;
   }
   auto load_stage = [&](int t) __attribute__((always_inline)) {
-    uint8_t* slot = smem + (t & 1) * C::STAGE;
+    uint8_t* slot = smem + (t % C::NBUF) * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const uint8_t* src = (is_x[i] ? x8 : w8) + goff[i] + (int64_t)t * C::BK;
@@ -160,50 +173,69 @@ __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  // Each wave waits for its own direct loads of tile t (vmcnt), leaving the
-  // loads of tile t+1 in flight, then a raw s_barrier (with a compiler memory
-  // clobber) publishes tile t to every wave; __syncthreads() would also wait
-  // for the loads of t+1.
-  const int nk = K / C::BK;
-  load_stage(0);
-  for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) {
-      load_stage(t + 1);
-      __builtin_amdgcn_s_waitcnt((C::CPT & 15) | (7 << 4) | (15 << 8) | ((C::CPT >> 4) << 14));
-    } else {
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    __asm__ volatile("s_barrier" ::: "memory");
-    const uint8_t* wt = smem + (t & 1) * C::STAGE;
+  // Software pipeline.  While the MFMAs of tile t run, the wave's LDS reads of
+  // tile t+1 fill the other fragment buffer.  At stage t each wave waits for
+  // its own direct loads of tile t+1 (vmcnt, leaving the two later tiles in
+  // flight) and for its LDS reads of tile t (lgkmcnt 0), then a raw s_barrier
+  // (compiler memory clobber) publishes tile t+1 and certifies that no wave
+  // still reads tile t's slot, which the loads of tile t+NBUF then refill.
+  // __syncthreads() would also wait for the loads still in flight.
+  auto read_frags = [&](int t, v8i (&af)[C::TN], v8i (&bf)[C::TM]) __attribute__((always_inline)) {
+    const uint8_t* wt = smem + (t % C::NBUF) * C::STAGE;
     const uint8_t* xt = wt + C::ACH * 16;
 #pragma unroll
-    for (int ks = 0; ks < C::BK / 64; ++ks) {
-      v8i af[C::TN], bf[C::TM];
-#pragma unroll
-      for (int a = 0; a < C::TN; ++a) {
-        const int r = n0 + 32 * a + l32;
-        const v4i lo = *(const v4i*)(wt + 16 * gk_pos(r, 4 * ks + 2 * half));
-        const v4i hi = *(const v4i*)(wt + 16 * gk_pos(r, 4 * ks + 2 * half + 1));
-        af[a] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b) {
-        const int r = m0 + 32 * b + l32;
-        const v4i lo = *(const v4i*)(xt + 16 * gk_pos(r, 4 * ks + 2 * half));
-        const v4i hi = *(const v4i*)(xt + 16 * gk_pos(r, 4 * ks + 2 * half + 1));
-        bf[b] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int a = 0; a < C::TN; ++a)
-#pragma unroll
-        for (int b = 0; b < C::TM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[a], bf[b], acc[a][b], 0, 0,
-                                                                     0, 0, 0, 0);
+    for (int a = 0; a < C::TN; ++a) {
+      const int r = n0 + 32 * a + l32;
+      const v4i lo = *(const v4i*)(wt + 16 * gk_pos(r, 2 * half));
+      const v4i hi = *(const v4i*)(wt + 16 * gk_pos(r, 2 * half + 1));
+      af[a] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    // every wave's reads of this slot have returned (the MFMAs consumed them)
-    // before the next iteration's loads refill it
-    __asm__ volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int b = 0; b < C::TM; ++b) {
+      const int r = m0 + 32 * b + l32;
+      const v4i lo = *(const v4i*)(xt + 16 * gk_pos(r, 2 * half));
+      const v4i hi = *(const v4i*)(xt + 16 * gk_pos(r, 2 * half + 1));
+      bf[b] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  auto mfmas = [&](const v8i (&af)[C::TN], const v8i (&bf)[C::TM]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < C::TN; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[a], bf[b], acc[a][b], 0, 0, 0,
+                                                                   0, 0, 0);
+  };
+  constexpr int WAIT2 = (2 * C::CPT & 15) | (7 << 4) | (0 << 8) | ((2 * C::CPT >> 4) << 14);
+  constexpr int WAIT3 = (3 * C::CPT & 15) | (7 << 4) | (0 << 8) | ((3 * C::CPT >> 4) << 14);
+  const int nk = K / C::BK;
+#pragma unroll
+  for (int i = 0; i < C::NBUF; ++i)
+    if (i < nk) load_stage(i);
+  if (nk >= C::NBUF) __builtin_amdgcn_s_waitcnt(WAIT3);
+  else __builtin_amdgcn_s_waitcnt(0);
+  __asm__ volatile("s_barrier" ::: "memory");
+  v8i afA[C::TN], bfA[C::TM], afB[C::TN], bfB[C::TM];
+  read_frags(0, afA, bfA);
+  // one stage; cur holds tile t's fragments, nxt receives tile t+1's
+  auto stage = [&](int t, const v8i (&af)[C::TN], const v8i (&bf)[C::TM], v8i (&an)[C::TN],
+                   v8i (&bn)[C::TM]) __attribute__((always_inline)) {
+    if (t + 1 < nk) {
+      // loads issued so far: tiles <= t + NBUF - 1; tile t+1 must have landed
+      if (t + 3 < nk) __builtin_amdgcn_s_waitcnt(WAIT2);
+      else __builtin_amdgcn_s_waitcnt(0);
+      __asm__ volatile("s_barrier" ::: "memory");
+      if (t + C::NBUF < nk) load_stage(t + C::NBUF);
+      read_frags(t + 1, an, bn);
+    }
+    mfmas(af, bf);
+  };
+  int t = 0;
+  for (; t + 1 < nk; t += 2) {
+    stage(t, afA, bfA, afB, bfB);
+    stage(t + 1, afB, bfB, afA, bfA);
   }
+  if (t < nk) stage(t, afA, bfA, afB, bfB);
 
   // ---- epilogue: out[m][n] = bf16((acc * sx[m]) * sw[n] + bias[n]) ----
   // accumulator register i of tile (a, b): n = n0 + 32 a + 8 (i / 4) + 4 half + i % 4,

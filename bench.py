@@ -48,11 +48,11 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_src, workload, q_block, k_block):
+def traffic_record(kernel_src, workload, q_block=32, k_block=64, kernel="attn_fwd"):
     """HBM traffic per launch from the committed counter summary of this
-    workload, if it was taken on the current kernel source with the same
-    scale granularities (else None)."""
-    p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_counters.json")
+    kernel and workload, if it was taken on the current kernel source with the
+    same scale granularities (else None)."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
@@ -206,7 +206,9 @@ def run_projection(args, torch, synth, sage):
         "roofline": {"kernel": "sage_gemm_fp8_rowwise (gemm_fp8_kernel: 256 x 256 blocks, 8 waves)",
                      "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic_record(os.path.join(ROOT, "quantized_attention_video_smooth_amd",
+                                                            "csrc", "sage_proj.hip"), "vmlp_proj",
+                                               kernel="gemm_fp8")},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = proj_cpu_baseline(M, K, N, args.seed)

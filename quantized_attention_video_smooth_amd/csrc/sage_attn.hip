@@ -68,7 +68,7 @@ struct AttnCfg {
   // tiles loaded ahead of the one in softmax: two workgroups per CU keep
   // three in flight within the same LDS budget per CU
   static constexpr int AHEAD = NW == 8 ? 2 : 3;
-  static constexpr int NBUF = AHEAD + 1;         // LDS ring depth (tiles t .. t+AHEAD)
+  static constexpr int NBUF = 4;                 // LDS ring depth (>= AHEAD + 1; a power of two)
   static constexpr int CPT = (KCH + VCH) / NT;  // direct-load instructions per wave per tile
   static_assert(CPT * NT == KCH + VCH, "tile copy must split evenly");
 };
@@ -165,13 +165,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
       goff[i] = d * Np + c * 16;
     }
   }
-  auto gload_lds = [&](int t) __attribute__((always_inline)) {
-    uint8_t* slot = smem + (t % C::NBUF) * C::STAGE;
+  auto gload_lds = [&](int t, int sl) __attribute__((always_inline)) {
+    uint8_t* slot = smem + sl * C::STAGE;
+    const uint8_t* vt = vbase + (size_t)t * 64;       // wave-uniform tile bases
+    const uint8_t* kt = (const uint8_t*)kbase + (size_t)t * 64 * D;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int wbase = (i * C::NW + wave) * 64 * 16;  // this wave's LDS bytes in the slot
-      const uint8_t* src = is_v(i) ? (const uint8_t*)vbase + (size_t)t * 64 + goff[i]
-                                   : (const uint8_t*)kbase + (size_t)t * 64 * D + goff[i];
+      const uint8_t* src = is_v(i) ? vt + (uint32_t)goff[i] : kt + (uint32_t)goff[i];
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(slot + wbase), 16, 0, 0);
     }
@@ -189,9 +190,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 #pragma unroll
   for (int j = 0; j < KPT; ++j) ksc_cur[j] = ksc[j];
 
-  // S^T(t) = K(t) Q^T into sdst (operands read from LDS slot t % 3).
-  auto qk_mfma = [&](int t, v16i (&sdst)[2]) __attribute__((always_inline)) {
-    const uint8_t* ks = smem + (t % C::NBUF) * C::STAGE;
+  // S^T(t) = K(t) Q^T into sdst (operands read from LDS slot sl = t % NBUF).
+  auto qk_mfma = [&](int sl, v16i (&sdst)[2]) __attribute__((always_inline)) {
+    const uint8_t* ks = smem + sl * C::STAGE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sdst[kb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -203,8 +204,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     }
   };
   // V^T(t) operands from LDS, and O^T += V^T(t) P^T(t).
-  auto load_v = [&](int t, v8i (&vop)[C::DC]) __attribute__((always_inline)) {
-    const uint8_t* vs = smem + (t % C::NBUF) * C::STAGE + C::KBYTES;
+  auto load_v = [&](int sl, v8i (&vop)[C::DC]) __attribute__((always_inline)) {
+    const uint8_t* vs = smem + sl * C::STAGE + C::KBYTES;
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc) {
       const v4i lo = *(const v4i*)(vs + 16 * v_pos(32 * dc + l32, 2 * half));
@@ -325,13 +326,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   // next_tag: std::true_type when tile t+1 exists (its S^T MFMAs are issued
   // here, in the same basic block as the softmax, so the two can interleave),
   // std::false_type for the last tile.
-  auto step = [&](int t, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag, auto next_tag)
+  // u: t % NBUF (a compile-time constant in the unrolled main loop)
+  auto step = [&](int t, int u, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag, auto next_tag)
       __attribute__((always_inline)) {
     const bool issue = t + C::AHEAD < ntiles;
-    if (issue) gload_lds(t + C::AHEAD);
-    if constexpr (decltype(next_tag)::value) qk_mfma(t + 1, snext);
+    if (issue) gload_lds(t + C::AHEAD, (u + C::AHEAD) % C::NBUF);
+    if constexpr (decltype(next_tag)::value) qk_mfma((u + 1) % C::NBUF, snext);
     v8i vop[C::DC];
-    load_v(t, vop);
+    load_v(u, vop);
     softmax(t, scur, masked_tag);
     pv_mfma(vop);
     if (issue && C::AHEAD > 2) __builtin_amdgcn_s_waitcnt(kWaitLgkm0VmCpt<C::CPT>);
@@ -342,29 +344,39 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   // ---- prologue: tiles 0 .. AHEAD-1 in LDS, S^T(0) issued ----
 #pragma unroll
   for (int i = 0; i < C::AHEAD; ++i)
-    if (i < ntiles) gload_lds(i);
+    if (i < ntiles) gload_lds(i, i);
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
   v16i sA[2], sB[2];
   qk_mfma(0, sA);
 
-  // ---- key loop, unrolled by two so the S buffers alternate statically ----
-  // Main loop: pairs of tiles followed by at least one more tile (all such
-  // tiles are full: only the last tile can hold padding).  One or two tiles
-  // remain after it; the last of them is padded when N % 64 != 0.
+  // ---- key loop ----
+  // Main loop: groups of four tiles followed by at least one more tile (all
+  // such tiles are full: only the last tile can hold padding), unrolled by the
+  // ring depth so that every step's LDS slot is a constant (the slot base
+  // becomes an instruction offset instead of a per-read address add) and the
+  // S buffers alternate statically.  Then pairs, then one or two last tiles;
+  // the last of them is padded when N % 64 != 0.
   const int nfull = N / 64;  // tiles without padding keys
   int t = 0;
+  // unrolled by the ring depth: the slot of every step is a constant
+  for (; t + 4 < ntiles; t += 4) {
+    step(t, 0, sA, sB, std::false_type{}, std::true_type{});
+    step(t + 1, 1, sB, sA, std::false_type{}, std::true_type{});
+    step(t + 2, 2, sA, sB, std::false_type{}, std::true_type{});
+    step(t + 3, 3, sB, sA, std::false_type{}, std::true_type{});
+  }
   for (; t + 2 < ntiles; t += 2) {
-    step(t, sA, sB, std::false_type{}, std::true_type{});
-    step(t + 1, sB, sA, std::false_type{}, std::true_type{});
+    step(t, t % C::NBUF, sA, sB, std::false_type{}, std::true_type{});
+    step(t + 1, (t + 1) % C::NBUF, sB, sA, std::false_type{}, std::true_type{});
   }
   auto last_step = [&](int t, v16i (&scur)[2], v16i (&snext)[2]) __attribute__((always_inline)) {
-    if (t < nfull) step(t, scur, snext, std::false_type{}, std::false_type{});
-    else step(t, scur, snext, std::true_type{}, std::false_type{});
+    if (t < nfull) step(t, t % C::NBUF, scur, snext, std::false_type{}, std::false_type{});
+    else step(t, t % C::NBUF, scur, snext, std::true_type{}, std::false_type{});
   };
   // t is even here: S^T(t) is in sA
   if (t + 1 < ntiles) {
-    step(t, sA, sB, std::false_type{}, std::true_type{});
+    step(t, t % C::NBUF, sA, sB, std::false_type{}, std::true_type{});
     last_step(t + 1, sB, sA);
   } else {
     last_step(t, sA, sB);

@@ -45,7 +45,9 @@ def build() -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+    # -z defs: an unresolved symbol (e.g. a kernel launch stub the host pass
+    # failed to emit) fails the link here instead of the first dlopen
+    subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs],
                    check=True, capture_output=True)
     os.replace(tmp, LIB)
     return LIB

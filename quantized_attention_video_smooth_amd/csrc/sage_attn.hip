@@ -165,16 +165,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
       goff[i] = d * Np + c * 16;
     }
   }
+  // Loads address this head's K (Np*D bytes) and V^T (D*Np bytes) as buffers:
+  // lane offset goff[i], tile offset t*64*D (K) or t*64 (V^T), both below the
+  // record count for every t < ntiles.
   auto gload_lds = [&](int t, int sl) __attribute__((always_inline)) {
     uint8_t* slot = smem + sl * C::STAGE;
-    const uint8_t* vt = vbase + (size_t)t * 64;       // wave-uniform tile bases
-    const uint8_t* kt = (const uint8_t*)kbase + (size_t)t * 64 * D;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int wbase = (i * C::NW + wave) * 64 * 16;  // this wave's LDS bytes in the slot
-      const uint8_t* src = is_v(i) ? vt + (uint32_t)goff[i] : kt + (uint32_t)goff[i];
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(slot + wbase), 16, 0, 0);
+      void* dst = slot + wbase;
+      if (is_v(i))
+        lds_load16(vbase, D * Np, dst, goff[i], t * 64);
+      else
+        lds_load16(kbase, Np * D, dst, goff[i], t * 64 * D);
     }
   };
 

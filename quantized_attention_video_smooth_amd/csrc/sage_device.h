@@ -13,6 +13,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;  // every kernel runs 4 waves of 64 lanes
 
+// 16 bytes per lane from base + voff + soff straight into LDS at lds + 16 lane
+// (buffer_load_dwordx4 ... lds; lds wave-uniform).  The buffer resource spans
+// `bytes` bytes from `base` (word 3: 32-bit data format, no swizzle; reads past
+// the record count return zero), so the lane offset stays one 32-bit VGPR and
+// the uniform offset an SGPR, with no per-load address arithmetic.  Kept out
+// of kernel bodies: the host pass drops the launch stubs of a kernel whose body
+// names the resource type.
+__device__ __forceinline__ void lds_load16(const void* base, int bytes, void* lds, int voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 // bf16 bit pattern (low or high half of a 32-bit word) -> fp32, exact.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -62,21 +62,58 @@ def traffic_record(kernel_src, workload, q_block=32, k_block=64, kernel="attn_fw
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_info():
+    """The CPU the oracle baseline ran on: model name, logical CPUs, and the
+    CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+# (query, key, head) pairs of tiled oracle attention in the baseline sample:
+# about 14 s on 16 host cores at the rate measured for the FLUX sample
+ORACLE_SAMPLE_PAIRS = 6.0e8
+
+
 def cpu_baseline(workload_cfg, seed=0):
-    """The oracle as it stands, on a bounded sample of the same workload:
-    full Q/K and V quantisation plus the tiled attention for every 18th
-    32-query block of every head; scaled to a whole-step estimate."""
+    """The oracle as it stands, on a bounded sample of the same workload: full
+    Q/K and V quantisation, plus the tiled attention for every s-th 32-query
+    block of every head, s chosen so the sample holds about
+    ORACLE_SAMPLE_PAIRS (query, key, head) pairs; scaled to a whole-step
+    estimate.  The quantisation is also timed on one thread."""
     import numpy as np
     import oracle
     import synth
     cfg = workload_cfg
     q, k, v = synth.make_qkv(cfg, seed)
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     qk = oracle.quant_qk(q, k)
     vq = oracle.quant_v(v)
     t_quant = time.perf_counter() - t0
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.quant_qk(q, k)
+        oracle.quant_v(v)
+        t_quant1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
     nb = math.ceil(cfg.N / 32)
-    blocks = list(range(0, nb, 18))
+    pairs_per_block = 32.0 * cfg.N * cfg.B * cfg.H
+    stride = max(1, math.ceil(nb * pairs_per_block / ORACLE_SAMPLE_PAIRS))
+    blocks = list(range(0, nb, stride))
     rows = np.array([r for b in blocks for r in range(32 * b, min(cfg.N, 32 * b + 32))], np.int32)
     t0 = time.perf_counter()
     oracle.attn_tiled(qk, vq, rows=rows)
@@ -86,12 +123,99 @@ def cpu_baseline(workload_cfg, seed=0):
     return {
         "value": round(ops / est / 1e12, 6),
         "unit": "TFLOPS",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"full Q/K/V quantisation ({t_quant:.2f} s) + tiled attention on "
-                   f"{rows.size}/{cfg.N} query rows of all {cfg.B * cfg.H} heads "
-                   f"({t_attn:.2f} s), scaled to the whole step ({est:.1f} s est.)"),
+        "sample": (f"full Q/K/V quantisation ({t_quant:.2f} s on {threads} threads, {t_quant1:.2f} s "
+                   f"on 1) + tiled attention on one 32-query block in {stride}: {rows.size}/{cfg.N} "
+                   f"query rows of all {cfg.B * cfg.H} heads ({t_attn:.2f} s), scaled to the whole "
+                   f"step ({est:.1f} s est.)"),
+        "quant_s": round(t_quant, 3),
+        "quant_1thread_s": round(t_quant1, 3),
+        "host": host_info(),
     }
+
+
+class GpuStateSampler:
+    """Samples the GPU's current shader clock, memory clock and socket power
+    from sysfs every `period` seconds on a thread: the starred (current) level
+    of pp_dpm_sclk / pp_dpm_mclk and hwmon power1_input (microwatts) of the
+    first DRM card that has them.  No child process: the bench process holds
+    the GPU."""
+
+    def __init__(self, period=0.02):
+        import glob
+        import threading
+        self.period = period
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.dev = os.path.dirname(cards[0]) if cards else None
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _starred_mhz(path):
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    tok = line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                    return float(tok.replace("mhz", ""))
+        return None
+
+    def _read(self):
+        import glob
+        sclk = self._starred_mhz(os.path.join(self.dev, "pp_dpm_sclk"))
+        mclk = self._starred_mhz(os.path.join(self.dev, "pp_dpm_mclk"))
+        power = None
+        for h in sorted(glob.glob(os.path.join(self.dev, "hwmon", "hwmon*", "power1_input"))):
+            with open(h) as f:
+                power = int(f.read().strip()) * 1e-6
+            break
+        return sclk, mclk, power
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except (OSError, ValueError, IndexError):
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.dev:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.dev:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return {"source": "sysfs", "samples": 0, "note": "no readable pp_dpm_sclk on this host"}
+
+        def stats(i, nd=0):
+            xs = sorted(x[i] for x in self.samples if x[i] is not None)
+            if not xs:
+                return None
+            return {"min": round(xs[0], nd), "median": round(xs[len(xs) // 2], nd), "max": round(xs[-1], nd)}
+
+        return {"source": f"sysfs {self.dev}: pp_dpm_sclk, pp_dpm_mclk (starred level), "
+                          "hwmon power1_input", "samples": len(self.samples),
+                "sclk_mhz": stats(0), "mclk_mhz": stats(1), "socket_power_w": stats(2)}
+
+
+def gpu_state_during(run_step, torch, seconds=1.0):
+    """Clock and power while the step runs back to back for `seconds` (a pass
+    of its own, after the timed steps)."""
+    with GpuStateSampler() as smp:
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                run_step()
+            torch.cuda.synchronize()
+    return smp.summary()
 
 
 def copy_calibration(torch, dev):
@@ -131,6 +255,7 @@ def proj_cpu_baseline(M, K, N, seed=0):
         "sample": (f"row quantisation of X in full ({t_q:.2f} s) + the scaled GEMM on "
                    f"{rows.size} x {cols.size} of the {M} x {N} outputs ({t_g:.2f} s), scaled "
                    f"to the whole step ({est:.1f} s est.)"),
+        "host": host_info(),
     }
 
 
@@ -210,6 +335,7 @@ def run_projection(args, torch, synth, sage):
                                                             "csrc", "sage_proj.hip"), "vmlp_proj",
                                                kernel="gemm_fp8")},
     }
+    res["gpu_state"] = gpu_state_during(step, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = proj_cpu_baseline(M, K, N, args.seed)
     return res
@@ -442,6 +568,7 @@ def main():
         "quant_v_gbs": round(work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9, 1),
         "roofline": roofline,
     }
+    res["gpu_state"] = gpu_state_during(step, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
     if args.copy_calibration:

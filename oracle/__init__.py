@@ -74,6 +74,7 @@ def _load():
         "orc_gemm_fp8_rowwise": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
                                   _vp, _vp, _vp], None),
         "orc_num_threads": ([], _i32),
+        "orc_set_num_threads": ([_i32], None),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -99,6 +100,12 @@ def _bf16_view(t):
 
 def num_threads() -> int:
     return _load().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (for timing; results do not
+    depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---- codecs --------------------------------------------------------------

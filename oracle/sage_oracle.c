@@ -621,3 +621,12 @@ int orc_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Thread count of the OpenMP loops above (timing only; no result depends on it). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

@@ -1,0 +1,55 @@
+"""Host-side pieces of bench.py: the GPU clock / power sampler's sysfs parsing
+and the oracle-baseline sample sizing (no GPU needed)."""
+import math
+import os
+
+import bench
+
+
+def _fake_card(tmp_path, sclk, mclk, power_uw):
+    dev = tmp_path / "device"
+    (dev / "hwmon" / "hwmon0").mkdir(parents=True)
+    (dev / "pp_dpm_sclk").write_text(sclk)
+    (dev / "pp_dpm_mclk").write_text(mclk)
+    (dev / "hwmon" / "hwmon0" / "power1_input").write_text(f"{power_uw}\n")
+    return str(dev)
+
+
+def test_sampler_reads_starred_levels_and_power(tmp_path):
+    # the formats the amdgpu driver prints: an "S:" line for the current
+    # shader clock when it sits between levels, else a starred level
+    dev = _fake_card(tmp_path, "S: 2104Mhz *\n0: 500Mhz\n1: 2400Mhz\n", "0: 2000Mhz *\n", 250000000)
+    smp = bench.GpuStateSampler()
+    smp.dev = dev
+    assert smp._read() == (2104.0, 2000.0, 250.0)
+    dev2 = _fake_card(tmp_path / "b", "0: 500Mhz\n1: 2400Mhz *\n", "0: 1900Mhz *\n", 1)
+    smp.dev = dev2
+    assert smp._read() == (2400.0, 1900.0, 1e-6)
+
+
+def test_sampler_summary(tmp_path):
+    smp = bench.GpuStateSampler()
+    smp.dev = "/x"
+    smp.samples = [(2100.0, 2000.0, 900.0), (2400.0, 2000.0, 1000.0), (2300.0, 2000.0, 950.0)]
+    s = smp.summary()
+    assert s["samples"] == 3
+    assert s["sclk_mhz"] == {"min": 2100.0, "median": 2300.0, "max": 2400.0}
+    assert s["socket_power_w"]["median"] == 950.0
+    smp.samples = []
+    assert bench.GpuStateSampler.summary(smp)["samples"] == 0
+
+
+def test_oracle_sample_stride_targets_a_bounded_sample():
+    # FLUX joint: every 2nd of 144 blocks; Long T2V: 15 of 1024 blocks
+    for (B, N, H), want in (((2, 4608, 24), 2), ((1, 32760, 40), 72)):
+        nb = math.ceil(N / 32)
+        stride = max(1, math.ceil(nb * 32.0 * N * B * H / bench.ORACLE_SAMPLE_PAIRS))
+        assert stride == want
+        rows = 32 * len(range(0, nb, stride))
+        assert rows * N * B * H <= 1.1 * bench.ORACLE_SAMPLE_PAIRS
+
+
+def test_host_info_fields():
+    h = bench.host_info()
+    assert set(h) == {"cpu_model", "logical_cpus", "usable_cpus"}
+    assert h["usable_cpus"] >= 1 and h["logical_cpus"] >= h["usable_cpus"]

@@ -17,7 +17,8 @@
 // (8 accumulator tiles).  K advances in 64-byte steps through a four-slot LDS
 // ring, three stages ahead, filled by direct global->LDS loads, with the
 // 16-byte chunks of each row XOR-swizzled so the operand reads are free of
-// bank conflicts.
+// bank conflicts.  The bf16 output block is staged in the same LDS and
+// written out in whole 512-byte rows.
 #include <hip/hip_runtime.h>
 
 #include "sage_device.h"
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
     const uint8_t* __restrict__ x8, const float* __restrict__ sx, int M,
     const uint8_t* __restrict__ w8, const float* __restrict__ sw, int N, int K,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int64_t ldo, int n_mblk,
-    int total) {
+    int total, int vec16) {
   using C = GemmCfg;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NBUF * C::STAGE];
 
@@ -239,19 +240,29 @@ __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
 
   // ---- epilogue: out[m][n] = bf16((acc * sx[m]) * sw[n] + bias[n]) ----
   // accumulator register i of tile (a, b): n = n0 + 32 a + 8 (i / 4) + 4 half + i % 4,
-  // m = m0 + 32 b + l32.
+  // m = m0 + 32 b + l32.  The bf16 block goes through LDS (the ring is free
+  // once every wave's last operand reads are consumed): row m_loc, 16-byte
+  // chunk c of its 512 bytes at chunk position c ^ (m_loc % 32), so the 32
+  // rows one store instruction touches and the 32 chunks one read touches
+  // spread over the banks.  It then leaves in whole rows: 32 lanes x 16 bytes
+  // per row.
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ volatile("s_barrier" ::: "memory");
+  constexpr int ROWB = C::BN * 2;  // bytes of one block row
+  static_assert(C::BM * ROWB <= C::NBUF * C::STAGE, "output block must fit the LDS ring");
 #pragma unroll
   for (int b = 0; b < C::TM; ++b) {
-    const int m = m_base + m0 + 32 * b + l32;
-    if (m >= M) continue;
-    const float sxm = sx[m];
-    uint16_t* orow = out + (int64_t)m * ldo;
+    const int m_loc = m0 + 32 * b + l32;
+    const int m = m_base + m_loc;
+    const float sxm = m < M ? sx[m] : 0.0f;
+    uint8_t* lrow = smem + m_loc * ROWB;
 #pragma unroll
     for (int a = 0; a < C::TN; ++a)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n_base + n0 + 32 * a + 8 * g + 4 * half;
-        if (n >= N) continue;  // N % 4 == 0: a group is all in or all out
+        const int n_loc = n0 + 32 * a + 8 * g + 4 * half;
+        const int n = n_base + n_loc;
+        if (n >= N) continue;  // N % 4 == 0: a group is all in or all out; never stored
         const float4 s4 = *(const float4*)(sw + n);
         float y[4];
         y[0] = acc[a][b][4 * g + 0] * sxm * s4.x;
@@ -265,8 +276,27 @@ __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
           y[2] += bf16_lo(bb.y);
           y[3] += bf16_hi(bb.y);
         }
-        *(uint2*)(orow + n) = make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
+        const int chunk = n_loc >> 3;
+        *(uint2*)(lrow + 16 * (chunk ^ (m_loc & 31)) + 8 * half) =
+            make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ volatile("s_barrier" ::: "memory");
+  constexpr int CPR = ROWB / 16;  // 16-byte chunks per block row
+#pragma unroll 4
+  for (int idx = tid; idx < C::BM * CPR; idx += C::NT) {
+    const int r = idx / CPR, c = idx % CPR;
+    const int m = m_base + r, n = n_base + 8 * c;
+    if (m >= M || n >= N) continue;
+    const uint4 v = *(const uint4*)(smem + r * ROWB + 16 * (c ^ (r & 31)));
+    uint16_t* dst = out + (int64_t)m * ldo + n;
+    if (vec16 && n + 8 <= N) {
+      *(uint4*)dst = v;
+    } else {
+      *(uint2*)dst = make_uint2(v.x, v.y);
+      if (n + 4 < N) *(uint2*)(dst + 4) = make_uint2(v.z, v.w);
+    }
   }
 }
 
@@ -300,7 +330,8 @@ hipError_t launch_gemm_fp8_rowwise(const uint8_t* x8, const float* sx, int M, co
   const int n_mblk = (int)ceil_div(M, GemmCfg::BM);
   const int total = n_mblk * (int)ceil_div(N, GemmCfg::BN);
   hipLaunchKernelGGL(gemm_fp8_kernel, dim3(grid), dim3(GemmCfg::NT), 0, stream, x8, sx, M, w8, sw,
-                     N, K, bias, out, ldo, n_mblk, total);
+                     N, K, bias, out, ldo, n_mblk, total,
+                     (int)(((uintptr_t)out % 16 == 0) && (ldo % 8 == 0)));
   return hipGetLastError();
 }
 

@@ -82,20 +82,25 @@ def test_gemm_small_full(sage, M, K, N, with_bias):
     assert e < 4e-3
 
 
-def test_gemm_into_a_column_slice(sage):
-    """The output written into columns [64, 64+N) of a wider buffer; the rest of
-    the buffer untouched."""
-    M, K, N = 130, 256, 200
+@pytest.mark.parametrize("N,extra,off", [(200, 128, 64), (200, 132, 4), (196, 132, 68)],
+                         ids=["ldo%8=0,16B-aligned", "ldo%8=4,8B-aligned", "N%8=4,ldo%8=0,8B-aligned"])
+def test_gemm_into_a_column_slice(sage, N, extra, off):
+    """The output written into columns [off, off+N) of a wider buffer (row
+    pitch N + extra elements): equal to the contiguous output, the rest of the
+    buffer untouched.  Covers 16-byte row stores and the 8-byte ones used when
+    the pitch or the base allows no more."""
+    M, K = 130, 256
+    _log(f"[proj] column slice N{N} pitch {N + extra} offset {off}")
     x, w, b = synth.proj_inputs(M, K, N, tag=630)
     xc, xs = sage.quant_rows_fp8(x.cuda())
     wc, ws = sage.quant_rows_fp8(w.cuda())
-    buf = torch.full((M, N + 128), 7.0, dtype=torch.bfloat16, device="cuda")
-    view = buf[:, 64:64 + N]
+    buf = torch.full((M, N + extra), 7.0, dtype=torch.bfloat16, device="cuda")
+    view = buf[:, off:off + N]
     sage.gemm_fp8_rowwise(xc, xs, wc, ws, bias=b.cuda(), out=view)
     ref_out = sage.gemm_fp8_rowwise(xc, xs, wc, ws, bias=b.cuda())
     torch.cuda.synchronize()
     assert torch.equal(view, ref_out)
-    assert torch.all(buf[:, :64] == 7) and torch.all(buf[:, 64 + N:] == 7)
+    assert torch.all(buf[:, :off] == 7) and torch.all(buf[:, off + N:] == 7)
 
 
 def test_vmlp_projection_sampled_and_v_alias(sage):

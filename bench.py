@@ -539,9 +539,12 @@ def main():
         qv_bytes = work["quant_q_bytes"] + work["quant_k_bytes"] + work["quant_v_bytes"]
         value = qv_bytes / step_s / 1e9
         gbs = (work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9
-        roofline = {"kernel": "sage_quant_qk", "bound": "hbm", "achieved": round(gbs, 1),
+        roofline = {"kernel": "sage_quant_qk (stats_kernel, finalize_kernel, qk_quant_kernel)",
+                    "bound": "hbm", "achieved": round(gbs, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                    "traffic": None}
+                    "traffic": traffic_record(os.path.join(ROOT, "quantized_attention_video_smooth_amd",
+                                                           "csrc", "sage_quant.hip"), cfg.name, qb, kbl,
+                                              kernel="quant_qk")}
         unit = "GB/s"
 
     res = {

@@ -335,7 +335,8 @@ def run_projection(args, torch, synth, sage):
                                                             "csrc", "sage_proj.hip"), "vmlp_proj",
                                                kernel="gemm_fp8")},
     }
-    res["gpu_state"] = gpu_state_during(step, torch)
+    if args.gpu_state_seconds > 0:
+        res["gpu_state"] = gpu_state_during(step, torch, args.gpu_state_seconds)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = proj_cpu_baseline(M, K, N, args.seed)
     return res
@@ -362,6 +363,9 @@ def main():
                          "sage_norm_rope_quant_qk, 'composed' runs sage_norm_rope on Q and on K "
                          "(bf16 NHD stores) and then sage_quant_qk_ex; 'none' (default) quantises "
                          "Q and K as given")
+    ap.add_argument("--gpu-state-seconds", type=float, default=1.0,
+                    help="length of the pass of back-to-back steps during which the GPU clock and power "
+                         "are sampled (0: no such pass, e.g. under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the run, copy 256 MiB device to device once: a kernel of known "
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counter readings")
@@ -571,7 +575,8 @@ def main():
         "quant_v_gbs": round(work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9, 1),
         "roofline": roofline,
     }
-    res["gpu_state"] = gpu_state_during(step, torch)
+    if args.gpu_state_seconds > 0:
+        res["gpu_state"] = gpu_state_during(step, torch, args.gpu_state_seconds)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
     if args.copy_calibration:

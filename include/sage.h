@@ -164,6 +164,22 @@ int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                      void* stream);
 
 /*
+ * sage_quant_q -- the Q half of sage_quant_qk_ex alone.  Q's codes and scales
+ * depend only on Q's own blocks (no statistics over the sequence), so under
+ * sequence parallelism (the "FLUX 3 Action" SGLang page, §3.1 Multi-GPU: the
+ * joint sequence is split and K/V are gathered) each rank quantises its own
+ * token shard of Q with this call and feeds it to sage_attn_fwd_shard.
+ * Inputs (device): q bf16 [B,N,H,D] with element strides (q_sb, q_sn, q_sh).
+ * Outputs (device, contiguous, written in full including padding):
+ *   q_i8 int8 [B,H,Np,D], q_scale fp32 [B,H,Np/q_block], q_block = SAGE_Q_BLOCK
+ *   or SAGE_Q_TOKEN; bit-identical to the Q outputs of sage_quant_qk_ex for the
+ *   same Q.  No workspace.  Errors as sage_quant_qk_ex.
+ */
+int sage_quant_q(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                 int B, int N, int H, int D, int8_t* q_i8, float* q_scale, int q_block,
+                 void* stream);
+
+/*
  * sage_norm_rope -- the QK RMSNorm + RoPE producer of Q or K ("FLUX 3 Action"
  * SGLang page: a fused QK RMSNorm + RoPE, 4-axis RoPE), storing BF16 NHD
  * directly (report card B).  Per token row x of a head, with weights w and
@@ -268,6 +284,31 @@ int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
                      void* stream);
 
 /*
+ * sage_attn_fwd_shard -- sage_attn_fwd_ex for Nq queries against Nk keys: the
+ * attention of one rank under sequence parallelism (the "FLUX 3 Action"
+ * SGLang page, §3.1 Multi-GPU: the joint sequence is split and K/V are
+ * gathered), i.e. its own query shard against the whole gathered sequence.
+ * Inputs (device):
+ *   q_i8 int8 [B,H,Npq,D], q_scale fp32 [B,H,Npq/q_block]  (Npq = padded Nq),
+ *     e.g. from sage_quant_q on the rank's Q shard;
+ *   k_i8 int8 [B,H,Npk,D], k_scale fp32 [B,H,Npk/k_block], v_fp8 uint8
+ *     [B,H,D,Npk], v_scale / v_mean fp32 [B,H,D]  (Npk = padded Nk): the
+ *     quantised K and V of the whole sequence.
+ * Output (device): out bf16 [B,Nq,H,D] with element strides (o_sb, o_sn, o_sh).
+ * Query row i of the shard is computed exactly as row i0 + i of sage_attn_fwd_ex
+ * over the whole sequence when the shard starts at token i0 (a multiple of
+ * q_block) and its Q codes and scales are that sequence's: the key loop, its
+ * tile order and every rounding are the same.  Nq == Nk is sage_attn_fwd_ex.
+ * Errors as sage_attn_fwd_ex, with both Nq and Nk checked.
+ */
+int sage_attn_fwd_shard(const int8_t* q_i8, const float* q_scale, int Nq,
+                        const int8_t* k_i8, const float* k_scale,
+                        const uint8_t* v_fp8, const float* v_scale, const float* v_mean, int Nk,
+                        int B, int H, int D, float sm_scale,
+                        void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block,
+                        int k_block, void* stream);
+
+/*
  * sage_quant_rows_fp8 -- row-wise E4M3 quantisation of a bf16 matrix (report
  * §02 stage 02; SGLang page: per-token activation scales, one scale per
  * weight output row).  For each row m of x (K values):
@@ -340,6 +381,16 @@ int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale,
                               int B, int N, int H, int D,
                               const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
                               int q_block, int k_block);
+
+int sage_validate_quant_q(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                          int B, int N, int H, int D, const int8_t* q_i8, const float* q_scale,
+                          int q_block);
+int sage_validate_attn_fwd_shard(const int8_t* q_i8, const float* q_scale, int Nq,
+                                 const int8_t* k_i8, const float* k_scale,
+                                 const uint8_t* v_fp8, const float* v_scale, const float* v_mean,
+                                 int Nk, int B, int H, int D,
+                                 const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                                 int q_block, int k_block);
 
 int sage_validate_norm_rope(const void* x, int64_t x_sb, int64_t x_sn, int64_t x_sh,
                             int B, int N, int H, int D,

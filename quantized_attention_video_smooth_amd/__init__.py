@@ -75,6 +75,12 @@ _SIGS = {
     "sage_validate_gemm_fp8_rowwise": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i64], _i32),
     "sage_validate_attn_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                    _vp, _i64, _i64, _i64, _i32, _i32], _i32),
+    "sage_quant_q": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp], _i32),
+    "sage_validate_quant_q": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32], _i32),
+    "sage_attn_fwd_shard": ([_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                             _vp, _i64, _i64, _i64, _i32, _i32, _vp], _i32),
+    "sage_validate_attn_fwd_shard": ([_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                      _i32, _vp, _i64, _i64, _i64, _i32, _i32], _i32),
     "sage_status_string": ([_i32], ctypes.c_char_p),
 }
 
@@ -131,6 +137,14 @@ def sage_attn_fwd_ex(*args) -> int:
 
 def sage_quant_rows_fp8(*args) -> int:
     return lib().sage_quant_rows_fp8(*args)
+
+
+def sage_quant_q(*args) -> int:
+    return lib().sage_quant_q(*args)
+
+
+def sage_attn_fwd_shard(*args) -> int:
+    return lib().sage_attn_fwd_shard(*args)
 
 
 def sage_gemm_fp8_rowwise(*args) -> int:
@@ -323,6 +337,23 @@ def quant_qk(q, k, stream=None, q_block: int = 32, k_block: int = 64):
     return q_i8, q_scale, k_i8, k_scale, k_mean
 
 
+def quant_q(q, stream=None, q_block: int = 32):
+    """INT8 Q alone (the Q half of quant_qk; e.g. one rank's token shard of Q).
+    Returns (q_i8 [B,H,Np,D], q_scale [B,H,Np/q_block])."""
+    import torch
+    B, N, H, D = q.shape
+    qs = _nhd(q, "q")
+    if q_block not in (1, BQ):
+        raise ValueError("q_block must be 32 or 1")
+    Np = sage_padded_tokens(N)
+    q_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=q.device)
+    q_scale = torch.empty((B, H, Np // q_block), dtype=torch.float32, device=q.device)
+    _check(sage_quant_q(q.data_ptr(), *qs, B, N, H, D, q_i8.data_ptr(), q_scale.data_ptr(), q_block,
+                        _stream_ptr(stream)),
+           "sage_quant_q")
+    return q_i8, q_scale
+
+
 def quant_v(v, stream=None):
     """V smoothing + FP8 E4M3 V, transposed and slot-permuted.  Returns
     (v_fp8 [B,H,D,Np] uint8, v_scale [B,H,D], v_mean [B,H,D])."""
@@ -373,6 +404,27 @@ def attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, N: int, sm_sc
                             float(sm_scale) if sm_scale else 0.0, out.data_ptr(), *os_, q_block, k_block,
                             _stream_ptr(stream)),
            "sage_attn_fwd_ex")
+    return out
+
+
+def attn_fwd_shard(q_i8, q_scale, Nq: int, k_i8, k_scale, v_fp8, v_scale, v_mean, Nk: int,
+                   sm_scale: float | None = None, out=None, stream=None):
+    """Nq queries (quantised Q shard, e.g. from quant_q) against the Nk keys of the
+    whole sequence (quantised K and V); returns bf16 [B,Nq,H,D] (or fills `out`).
+    Scale granularities follow the scale lengths as in attn_fwd."""
+    import torch
+    B, H, Npq, D = q_i8.shape
+    Npk = k_i8.shape[2]
+    q_block = Npq // q_scale.shape[-1]
+    k_block = Npk // k_scale.shape[-1]
+    if out is None:
+        out = torch.empty((B, Nq, H, D), dtype=torch.bfloat16, device=q_i8.device)
+    os_ = _nhd(out, "out")
+    _check(sage_attn_fwd_shard(q_i8.data_ptr(), q_scale.data_ptr(), Nq, k_i8.data_ptr(),
+                               k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
+                               v_mean.data_ptr(), Nk, B, H, D, float(sm_scale) if sm_scale else 0.0,
+                               out.data_ptr(), *os_, q_block, k_block, _stream_ptr(stream)),
+           "sage_attn_fwd_shard")
     return out
 
 

@@ -101,7 +101,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v_fp8, const float* __restrict__ v_scale,
-    const float* __restrict__ v_mean, int H, int N, int Np, int n_qtiles, int total_tiles,
+    const float* __restrict__ v_mean, int H, int Nq, int Npq, int Nk, int Npk, int n_qtiles,
+    int total_tiles,
     int q_block, float cq0, uint16_t* __restrict__ out, int64_t o_sb, int64_t o_sn, int64_t o_sh) {
   using C = AttnCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NBUF * C::STAGE];
@@ -120,25 +121,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int q0 = qt * C::QT + wave * 32;
-  const int ntiles = Np / 64;
+  const int ntiles = Npk / 64;
 
   // Q^T operand (B of the S^T MFMA): lane holds query q0+l32, d = 32*dc + 16*half .. +16.
   v4i qop[C::DC];
   float cq = 0.0f;
-  if (q0 < Np) {
-    const int8_t* qp = q_i8 + ((size_t)bh * Np + q0 + l32) * D + 16 * half;
+  if (q0 < Npq) {
+    const int8_t* qp = q_i8 + ((size_t)bh * Npq + q0 + l32) * D + 16 * half;
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc) qop[dc] = *(const v4i*)(qp + 32 * dc);
     // the scale of this lane's query: one per 32-query block (the whole
     // wave) or one per query (q_block == 1)
-    cq = q_scale[(size_t)bh * (Np / q_block) + (q0 + l32) / q_block] * cq0;
+    cq = q_scale[(size_t)bh * (Npq / q_block) + (q0 + l32) / q_block] * cq0;
   } else {
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc) qop[dc] = v4i{0, 0, 0, 0};
   }
 
-  const int8_t* kbase = k_i8 + (size_t)bh * Np * D;
-  const uint8_t* vbase = v_fp8 + (size_t)bh * D * Np;
+  const int8_t* kbase = k_i8 + (size_t)bh * Npk * D;
+  const uint8_t* vbase = v_fp8 + (size_t)bh * D * Npk;
   static_assert(KB == 64 || KB == 16, "K block is 64 or 16 tokens");
   constexpr int KPT = 64 / KB;  // K scales per key tile
   const float* ksc = k_scale + (size_t)bh * ntiles * KPT;
@@ -162,10 +163,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     } else {
       const int p = g - C::KCH, d = p >> 2, cx = p & 3;
       const int c = cx ^ ((d >> 2) & 3);
-      goff[i] = d * Np + c * 16;
+      goff[i] = d * Npk + c * 16;
     }
   }
-  // Loads address this head's K (Np*D bytes) and V^T (D*Np bytes) as buffers:
+  // Loads address this head's K (Npk*D bytes) and V^T (D*Npk bytes) as buffers:
   // lane offset goff[i], tile offset t*64*D (K) or t*64 (V^T), both below the
   // record count for every t < ntiles.
   auto gload_lds = [&](int t, int sl) __attribute__((always_inline)) {
@@ -175,9 +176,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
       const int wbase = (i * C::NW + wave) * 64 * 16;  // this wave's LDS bytes in the slot
       void* dst = slot + wbase;
       if (is_v(i))
-        lds_load16(vbase, D * Np, dst, goff[i], t * 64);
+        lds_load16(vbase, D * Npk, dst, goff[i], t * 64);
       else
-        lds_load16(kbase, Np * D, dst, goff[i], t * 64 * D);
+        lds_load16(kbase, Npk * D, dst, goff[i], t * 64 * D);
     }
   };
 
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 #pragma unroll
     for (int j = 0; j < KPT; ++j) ksc_next[j] = ksc[tn * KPT + j];
     // key index of scur[kb][i] inside the tile: 32*kb + 8*(i/4) + 4*half + i%4
-    const int nvalid = N - t * 64;  // keys at or beyond nvalid are padding
+    const int nvalid = Nk - t * 64;  // keys at or beyond nvalid are padding
     if constexpr (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
       m_tile = (float)xhalf_max(mxi) * c[0];
     } else {
       // integer max per 16-key block, then scaled (every multiplier >= 0);
-      // a block wholly beyond N (scale 0) must not contribute its 0
+      // a block wholly beyond Nk (scale 0) must not contribute its 0
       m_tile = -__builtin_inff();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -359,8 +360,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   // ring depth so that every step's LDS slot is a constant (the slot base
   // becomes an instruction offset instead of a per-read address add) and the
   // S buffers alternate statically.  Then pairs, then one or two last tiles;
-  // the last of them is padded when N % 64 != 0.
-  const int nfull = N / 64;  // tiles without padding keys
+  // the last of them is padded when Nk % 64 != 0.
+  const int nfull = Nk / 64;  // tiles without padding keys
   int t = 0;
   // unrolled by the ring depth: the slot of every step is a constant
   for (; t + 4 < ntiles; t += 4) {
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   const float l_tot = xhalf_sum(l_run);
   const float inv_l = 1.0f / l_tot;
   const int qi = q0 + l32;
-  if (qi < N) {
+  if (qi < Nq) {
     uint16_t* orow = out + (int64_t)b * o_sb + (int64_t)qi * o_sn + (int64_t)h * o_sh;
     const float* vsc = v_scale + (size_t)bh * D;
     const float* vmu = v_mean + (size_t)bh * D;
@@ -412,24 +413,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 template <int D, int NW, int KB>
 hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                        const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                       const float* v_mean, int B, int N, int H, int q_block, float sm_scale,
-                       uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                       const float* v_mean, int B, int Nq, int Nk, int H, int q_block,
+                       float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
                        hipStream_t stream) {
   using C = AttnCfg<D, NW>;
-  const int Np = (int)padded_tokens(N);
-  const int n_qtiles = (int)ceil_div(N, C::QT);
+  const int Npq = (int)padded_tokens(Nq), Npk = (int)padded_tokens(Nk);
+  const int n_qtiles = (int)ceil_div(Nq, C::QT);
   const int total = B * H * n_qtiles;
   const int grid = (int)ceil_div(total, 8) * 8;
   const float cq0 = sm_scale * kLog2e;
   hipLaunchKernelGGL((attn_fwd_kernel<D, NW, KB>), dim3(grid), dim3(C::NT), 0, stream, q_i8, q_scale,
-                     k_i8, k_scale, v_fp8, v_scale, v_mean, H, N, Np, n_qtiles, total, q_block, cq0,
+                     k_i8, k_scale, v_fp8, v_scale, v_mean, H, Nq, Npq, Nk, Npk, n_qtiles, total,
+                     q_block, cq0,
                      out, o_sb, o_sn, o_sh);
   return hipGetLastError();
 }
 
 // Eight-wave workgroups when the grid is at least 8 of them per CU deep,
 // else four-wave ones (measured on MI355X: FLUX-sized grids of ~3.4 per CU
-// run ~20% faster with four waves, 20-deep grids ~1% slower).
+// run ~20% faster with four waves, 20-deep grids ~1% slower).  N: queries.
 int attn_waves(int B, int N, int H) {
   static std::atomic<int> ncu_cache{0};
   int ncu = ncu_cache.load(std::memory_order_relaxed);
@@ -448,12 +450,13 @@ int attn_waves(int B, int N, int H) {
 template <int D, int KB>
 hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                     const float* v_mean, int B, int N, int H, int q_block, float sm_scale,
-                     uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, hipStream_t stream) {
-  if (attn_waves(B, N, H) == 8)
-    return attn_launch<D, 8, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H,
+                     const float* v_mean, int B, int Nq, int Nk, int H, int q_block,
+                     float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                     hipStream_t stream) {
+  if (attn_waves(B, Nq, H) == 8)
+    return attn_launch<D, 8, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H,
                                  q_block, sm_scale, out, o_sb, o_sn, o_sh, stream);
-  return attn_launch<D, 4, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H,
+  return attn_launch<D, 4, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H,
                                q_block, sm_scale, out, o_sb, o_sn, o_sh, stream);
 }
 
@@ -468,11 +471,11 @@ void attn_shape(int B, int N, int H, int D, int* waves, int* workgroups) {
 
 hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                           const float* v_mean, int B, int N, int H, int D, int q_block,
+                           const float* v_mean, int B, int Nq, int Nk, int H, int D, int q_block,
                            int k_block, float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn,
                            int64_t o_sh, hipStream_t stream) {
 #define SAGE_ATTN_IMPL(DD, KK)                                                                    \
-  attn_impl<DD, KK>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N, H, q_block,      \
+  attn_impl<DD, KK>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H, q_block, \
                     sm_scale, out, o_sb, o_sn, o_sh, stream)
   if (D == 128) return k_block == 16 ? SAGE_ATTN_IMPL(128, 16) : SAGE_ATTN_IMPL(128, 64);
   return k_block == 16 ? SAGE_ATTN_IMPL(64, 16) : SAGE_ATTN_IMPL(64, 64);

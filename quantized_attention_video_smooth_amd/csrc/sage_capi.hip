@@ -170,29 +170,39 @@ int sage_validate_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_s
   return SAGE_OK;
 }
 
-int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                              const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                              const float* v_mean, int B, int N, int H, int D, const void* out,
-                              int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block) {
+int sage_validate_attn_fwd_shard(const int8_t* q_i8, const float* q_scale, int Nq,
+                                 const int8_t* k_i8, const float* k_scale, const uint8_t* v_fp8,
+                                 const float* v_scale, const float* v_mean, int Nk, int B, int H,
+                                 int D, const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+                                 int q_block, int k_block) {
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !v_mean || !out)
     return SAGE_ERR_NULL;
-  int st = check_shape(B, N, H, D);
+  int st = check_shape(B, Nq, H, D);
   if (st != SAGE_OK) return st;
+  if ((st = check_shape(B, Nk, H, D)) != SAGE_OK) return st;
   if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
   if (k_block != SAGE_K_BLOCK && k_block != SAGE_K_FINE) return SAGE_ERR_UNSUPPORTED;
-  if ((st = check_strides(B, N, H, o_sb, o_sn, o_sh)) != SAGE_OK) return st;
+  if ((st = check_strides(B, Nq, H, o_sb, o_sn, o_sh)) != SAGE_OK) return st;
   if (!aligned16(q_i8) || !aligned16(k_i8) || !aligned16(v_fp8) || !aligned16(out) ||
       ((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u) ||
       ((uintptr_t)v_mean & 3u))
     return SAGE_ERR_ALIGN;
-  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
-  const Range outs[1] = {range_of(out, view_bytes(B, N, H, D, o_sb, o_sn, o_sh))};
-  const Range ins[7] = {range_of(q_i8, bh * Np * D),      range_of(q_scale, bh * (Np / q_block) * 4),
-                        range_of(k_i8, bh * Np * D),      range_of(k_scale, bh * (Np / k_block) * 4),
-                        range_of(v_fp8, bh * D * Np),     range_of(v_scale, bh * D * 4),
+  const int64_t Npq = padded_tokens(Nq), Npk = padded_tokens(Nk), bh = (int64_t)B * H;
+  const Range outs[1] = {range_of(out, view_bytes(B, Nq, H, D, o_sb, o_sn, o_sh))};
+  const Range ins[7] = {range_of(q_i8, bh * Npq * D),     range_of(q_scale, bh * (Npq / q_block) * 4),
+                        range_of(k_i8, bh * Npk * D),     range_of(k_scale, bh * (Npk / k_block) * 4),
+                        range_of(v_fp8, bh * D * Npk),    range_of(v_scale, bh * D * 4),
                         range_of(v_mean, bh * D * 4)};
   if (any_overlap(outs, 1, ins, 7)) return SAGE_ERR_OVERLAP;
   return SAGE_OK;
+}
+
+int sage_validate_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                              const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                              const float* v_mean, int B, int N, int H, int D, const void* out,
+                              int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block) {
+  return sage_validate_attn_fwd_shard(q_i8, q_scale, N, k_i8, k_scale, v_fp8, v_scale, v_mean, N, B,
+                                      H, D, out, o_sb, o_sn, o_sh, q_block, k_block);
 }
 
 int sage_validate_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
@@ -228,6 +238,29 @@ int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const
                           stream);
 }
 
+int sage_validate_quant_q(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, int B, int N,
+                          int H, int D, const int8_t* q_i8, const float* q_scale, int q_block) {
+  if (!q || !q_i8 || !q_scale) return SAGE_ERR_NULL;
+  int st = check_shape(B, N, H, D);
+  if (st != SAGE_OK) return st;
+  if (q_block != SAGE_Q_BLOCK && q_block != SAGE_Q_TOKEN) return SAGE_ERR_UNSUPPORTED;
+  if ((st = check_strides(B, N, H, q_sb, q_sn, q_sh)) != SAGE_OK) return st;
+  if (!aligned16(q) || !aligned16(q_i8) || ((uintptr_t)q_scale & 3u)) return SAGE_ERR_ALIGN;
+  const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
+  const Range outs[2] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / q_block) * 4)};
+  const Range ins[1] = {range_of(q, view_bytes(B, N, H, D, q_sb, q_sn, q_sh))};
+  if (any_overlap(outs, 2, ins, 1)) return SAGE_ERR_OVERLAP;
+  return SAGE_OK;
+}
+
+int sage_quant_q(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, int B, int N, int H, int D,
+                 int8_t* q_i8, float* q_scale, int q_block, void* stream) {
+  const int st = sage_validate_quant_q(q, q_sb, q_sn, q_sh, B, N, H, D, q_i8, q_scale, q_block);
+  if (st != SAGE_OK) return st;
+  return status_of(sage::launch_quant_q((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
+                                        B, N, H, D, q_block, q_i8, q_scale, (hipStream_t)stream));
+}
+
 int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N, int H, int D,
                  uint8_t* v_fp8, float* v_scale, float* v_mean, void* workspace,
                  size_t workspace_bytes, void* stream) {
@@ -239,19 +272,29 @@ int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B,
                                         (hipStream_t)stream));
 }
 
+int sage_attn_fwd_shard(const int8_t* q_i8, const float* q_scale, int Nq, const int8_t* k_i8,
+                        const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
+                        const float* v_mean, int Nk, int B, int H, int D, float sm_scale, void* out,
+                        int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block,
+                        void* stream) {
+  const int st = sage_validate_attn_fwd_shard(q_i8, q_scale, Nq, k_i8, k_scale, v_fp8, v_scale,
+                                              v_mean, Nk, B, H, D, out, o_sb, o_sn, o_sh, q_block,
+                                              k_block);
+  if (st != SAGE_OK) return st;
+  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / __builtin_sqrtf((float)D);
+  return status_of(sage::launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq,
+                                         Nk, H, D, q_block, k_block, sm_scale, (uint16_t*)out,
+                                         B > 1 ? o_sb : 0, o_sn, H > 1 ? o_sh : 0,
+                                         (hipStream_t)stream));
+}
+
 int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                      const float* v_mean, int B, int N, int H, int D, float sm_scale, void* out,
                      int64_t o_sb, int64_t o_sn, int64_t o_sh, int q_block, int k_block,
                      void* stream) {
-  const int st = sage_validate_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B,
-                                           N, H, D, out, o_sb, o_sn, o_sh, q_block, k_block);
-  if (st != SAGE_OK) return st;
-  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / __builtin_sqrtf((float)D);
-  return status_of(sage::launch_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, N,
-                                         H, D, q_block, k_block, sm_scale, (uint16_t*)out,
-                                         B > 1 ? o_sb : 0,
-                                         o_sn, H > 1 ? o_sh : 0, (hipStream_t)stream));
+  return sage_attn_fwd_shard(q_i8, q_scale, N, k_i8, k_scale, v_fp8, v_scale, v_mean, N, B, H, D,
+                             sm_scale, out, o_sb, o_sn, o_sh, q_block, k_block, stream);
 }
 
 int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,

@@ -83,18 +83,25 @@ hipError_t launch_norm_rope(const uint16_t* x, int64_t sb, int64_t sn, int64_t s
                             uint16_t* y, int64_t y_sb, int64_t y_sn, int64_t y_sh,
                             hipStream_t stream);
 
+// Q alone (the Q half of launch_quant_qk, no workspace).
+hipError_t launch_quant_q(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, int B, int N,
+                          int H, int D, int q_block, int8_t* q_i8, float* q_scale,
+                          hipStream_t stream);
+
 hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
                           int H, int D, uint8_t* v_fp8, float* v_scale, float* v_mean,
                           void* workspace, hipStream_t stream);
 
-// Waves per workgroup and grid size of the attention launch for these sizes.
+// Waves per workgroup and grid size of the attention launch for these sizes
+// (N: queries).
 void attn_shape(int B, int N, int H, int D, int* waves, int* workgroups);
 
+// Nq queries against Nk keys (Nq == Nk for self-attention over one sequence).
 hipError_t launch_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                           const float* v_mean, int B, int N, int H, int D, int q_block,
-                           int k_block, float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
-                           hipStream_t stream);
+                           const float* v_mean, int B, int Nq, int Nk, int H, int D, int q_block,
+                           int k_block, float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn,
+                           int64_t o_sh, hipStream_t stream);
 
 // Row-wise FP8 projections.
 hipError_t launch_quant_rows_fp8(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* codes,

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
     const uint16_t* __restrict__ k_mean, int8_t* __restrict__ q_i8, float* __restrict__ q_scale,
     int8_t* __restrict__ k_i8, float* __restrict__ k_scale, int q_block, int k_block,
     const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
-    const float* __restrict__ rope, double eps, const float* __restrict__ rk) {
+    const float* __restrict__ rope, double eps, const float* __restrict__ rk, int q_only) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
   constexpr int PASSES = 64 / RPP;
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void qk_quant_kernel(
   // most recently read heads (most likely still in the memory-side cache)
   // are re-read first
   const int t = blockIdx.x, bh = gridDim.y - 1 - blockIdx.y;
-  const bool is_q = blockIdx.z != 0;
+  const bool is_q = (blockIdx.z | q_only) != 0;  // q_only: a grid of Q tiles alone
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x, lr = tid / LPR, lc = tid - lr * LPR;
   const uint16_t* src = is_q ? q + (int64_t)b * q_sb + (int64_t)h * q_sh
@@ -562,7 +562,7 @@ hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t 
   hipLaunchKernelGGL((qk_quant_kernel<D, NR>), dim3(Np / 64, B * H, 2), dim3(kThreads), 0, stream,
                      q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, H, N, Np, (const uint16_t*)k_mean,
                      q_i8, q_scale, k_i8, k_scale, q_block, k_block, nr.wq, nr.wk, nr.rope, nr.eps,
-                     (const float*)rk);
+                     (const float*)rk, 0);
   return hipGetLastError();
 }
 
@@ -606,6 +606,22 @@ hipError_t launch_quant_qk(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_
   if (D == 128) return nr ? SAGE_QK_IMPL(128, true) : SAGE_QK_IMPL(128, false);
   return nr ? SAGE_QK_IMPL(64, true) : SAGE_QK_IMPL(64, false);
 #undef SAGE_QK_IMPL
+}
+
+hipError_t launch_quant_q(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, int B, int N,
+                          int H, int D, int q_block, int8_t* q_i8, float* q_scale,
+                          hipStream_t stream) {
+  const int Np = (int)padded_tokens(N);
+#define SAGE_Q_ONLY(DD)                                                                          \
+  hipLaunchKernelGGL((qk_quant_kernel<DD, false>), dim3(Np / 64, B * H, 1), dim3(kThreads), 0,     \
+                     stream, q, q_sb, q_sn, q_sh, (const uint16_t*)nullptr, (int64_t)0, (int64_t)0,  \
+                     (int64_t)0, H, N, Np, (const uint16_t*)nullptr, q_i8, q_scale, (int8_t*)nullptr, \
+                     (float*)nullptr, q_block, 64, (const uint16_t*)nullptr,                         \
+                     (const uint16_t*)nullptr, (const float*)nullptr, 0.0, (const float*)nullptr, 1)
+  if (D == 128) SAGE_Q_ONLY(128);
+  else SAGE_Q_ONLY(64);
+#undef SAGE_Q_ONLY
+  return hipGetLastError();
 }
 
 hipError_t launch_norm_rope(const uint16_t* x, int64_t sb, int64_t sn, int64_t sh, int B, int N,

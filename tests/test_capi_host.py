@@ -157,6 +157,50 @@ def test_ex_entry_points_granularity(sage):
     assert lib.sage_attn_fwd_ex(*aargs[:11], 0.0, *aargs[11:], 8, 64, None) == -3
 
 
+def test_shard_entry_points_validation(sage):
+    """sage_quant_q and sage_attn_fwd_shard: documented status codes before any
+    HIP call; the Q and K/V ranges are sized by Nq and Nk separately."""
+    lib = sage.lib()
+    big = 1 << 40
+    B, H, D = 1, 2, 64
+    Nq, Nk = 100, 1000
+    Npq, Npk = 128, 1024
+    qargs = [big, 0, H * D, D, B, Nq, H, D, 2 * big, 3 * big]
+    assert lib.sage_validate_quant_q(*qargs, 32) == 0
+    assert lib.sage_validate_quant_q(*qargs, 1) == 0
+    assert lib.sage_validate_quant_q(*qargs, 16) == -3
+    assert lib.sage_quant_q(*qargs, 16, None) == -3
+    bad = list(qargs); bad[8] = None
+    assert lib.sage_validate_quant_q(*bad, 32) == -1
+    bad = list(qargs); bad[7] = 96
+    assert lib.sage_validate_quant_q(*bad, 32) == -3
+    bad = list(qargs); bad[2] = 0                      # Nq > 1 with zero token stride
+    assert lib.sage_validate_quant_q(*bad, 32) == -4
+    bad = list(qargs); bad[9] = big + 8                # q_scale inside the input rows
+    assert lib.sage_validate_quant_q(*bad, 32) == -7
+
+    def aargs(nq=Nq, nk=Nk, out=8 * big, k_i8=3 * big):
+        return [big, 2 * big, nq, k_i8, 4 * big, 5 * big, 6 * big, 7 * big, nk, B, H, D,
+                out, nq * H * D, H * D, D]
+    assert lib.sage_validate_attn_fwd_shard(*aargs(), 32, 64) == 0
+    assert lib.sage_validate_attn_fwd_shard(*aargs(), 1, 16) == 0
+    assert lib.sage_validate_attn_fwd_shard(*aargs(), 8, 64) == -3
+    assert lib.sage_attn_fwd_shard(*aargs()[:12], 0.0, *aargs()[12:], 8, 64, None) == -3
+    assert lib.sage_validate_attn_fwd_shard(*aargs(nq=0), 32, 64) == -2
+    assert lib.sage_validate_attn_fwd_shard(*aargs(nk=0), 32, 64) == -2
+    # an output placed right after the K codes of Nk keys is fine; one inside them is not
+    k_bytes = B * H * Npk * D
+    assert lib.sage_validate_attn_fwd_shard(*aargs(out=3 * big + k_bytes), 32, 64) == 0
+    assert lib.sage_validate_attn_fwd_shard(*aargs(out=3 * big + k_bytes - 16), 32, 64) == -7
+    # the output spans Nq rows only: right after it may start K
+    o_bytes = (Nq - 1) * H * D * 2 + (H - 1) * D * 2 + D * 2
+    assert lib.sage_validate_attn_fwd_shard(*aargs(out=8 * big, k_i8=8 * big + o_bytes), 32, 64) == 0
+    # Nq == Nk is the self-attention check of sage_validate_attn_fwd_ex
+    same = aargs(nq=Nk, nk=Nk)
+    ex = [same[0], same[1], same[3], same[4], same[5], same[6], same[7], B, Nk, H, D, *same[12:]]
+    assert lib.sage_validate_attn_fwd_ex(*ex, 32, 64) == lib.sage_validate_attn_fwd_shard(*same, 32, 64) == 0
+
+
 def test_attn_launch_shape(sage):
     """Shallow grids (FLUX, B2 H24 N4608: 864 eight-wave workgroups, ~3.4 per
     CU) take four-wave workgroups; deep ones (B1 H40 N32760: 20 per CU) eight."""

@@ -349,6 +349,107 @@ def run_projection(args, torch, synth, sage):
     return res
 
 
+def sp_shard(N, P, rank):
+    """Token range of `rank` when the sequence is split P ways in shards of a
+    multiple of 64 tokens (the last shard takes the rest)."""
+    size = math.ceil(N / P / 64) * 64
+    a = rank * size
+    return a, min(N, a + size)
+
+
+def run_sp_share(args, torch, synth, sage, cfg):
+    """One rank's share of a P-way sequence-parallel step on this GPU: the
+    rank's Q shard quantised (sage_quant_q) and its queries against the K and V
+    codes of the whole sequence (sage_attn_fwd_shard).  K and V are quantised
+    once before the timed region: they stand for the codes the rank gathers.
+    Not in the step: the rank's K/V shard quantisation with all-reduced
+    statistics and the K/V all-gather, which need the other ranks."""
+    lib = sage.lib()
+    B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
+    P, rank = args.sp, args.sp_rank
+    a, b = sp_shard(N, P, rank)
+    if not (0 <= rank and a < N):
+        raise SystemExit(f"--sp-rank {rank} holds no tokens of N={N} split {P} ways")
+    Nq = b - a
+    dev = torch.device("cuda:0")
+    q, k, v = synth.make_qkv(cfg, args.seed, device=dev)
+    qb, kbl = args.q_block, args.k_block
+    kq = sage.quant_qk(q, k, q_block=qb, k_block=kbl)
+    vq = sage.quant_v(v)
+    qs = q[:, a:b]
+    Npq = sage.sage_padded_tokens(Nq)
+    q_i8 = torch.empty((B, H, Npq, D), dtype=torch.int8, device=dev)
+    q_scale = torch.empty((B, H, Npq // qb), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Nq, H, D), dtype=torch.bfloat16, device=dev)
+    sp_ = int(torch.cuda.current_stream().cuda_stream)
+    os_ = out.stride()[:3]
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        st = lib.sage_quant_q(qs.data_ptr(), *qs.stride()[:3], B, Nq, H, D, q_i8.data_ptr(),
+                              q_scale.data_ptr(), qb, sp_)
+        if evs:
+            evs[1].record()
+        st |= lib.sage_attn_fwd_shard(q_i8.data_ptr(), q_scale.data_ptr(), Nq, kq[2].data_ptr(),
+                                      kq[3].data_ptr(), vq[0].data_ptr(), vq[1].data_ptr(),
+                                      vq[2].data_ptr(), N, B, H, D, 0.0, out.data_ptr(), *os_, qb, kbl,
+                                      sp_)
+        if evs:
+            evs[2].record()
+        if st != 0:
+            raise RuntimeError(f"libsage call failed with status {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    per = {"quant_q": [], "attn_fwd_shard": []}
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        step(evs)
+        torch.cuda.synchronize()
+        per["quant_q"].append(evs[0].elapsed_time(evs[1]))
+        per["attn_fwd_shard"].append(evs[1].elapsed_time(evs[2]))
+    stat = {k2: {"avg": round(sum(v2) / len(v2), 5), "median": round(sorted(v2)[len(v2) // 2], 5),
+                 "min": round(min(v2), 5), "p90": round(sorted(v2)[min(len(v2) - 1, 9 * len(v2) // 10)], 5)}
+            for k2, v2 in per.items()}
+    ops = 4.0 * B * H * Nq * N * D
+    at = ops / (stat["attn_fwd_shard"]["avg"] * 1e-3) / 1e12
+    waves, wgs = sage.sage_attn_launch_shape(B, Nq, H, D)
+    res = {
+        "metric": METRIC,
+        "value": round(ops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 QK / fp8-e4m3 PV, fp32 softmax+accum",
+        "data": "synthetic (seeded counter-based normals, bf16 NHD)",
+        "config": {"workload": f"{cfg.name}, rank {rank} of a {P}-way sequence split", "B": B, "N": N,
+                   "H": H, "D": D, "queries": [a, b], "keys": N, "q_block": qb, "k_block": kbl,
+                   "not_in_step": "K/V shard quantisation with all-reduced statistics, K/V all-gather"},
+        "kernels_ms": stat,
+        "roofline": {"kernel": f"sage_attn_fwd_shard (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave "
+                               f"workgroups, {wgs} per launch)",
+                     "bound": "mfma", "achieved": round(at, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(at / PEAK_MFMA_TFLOPS, 4), "traffic": None},
+    }
+    if args.gpu_state_seconds > 0:
+        res["gpu_state"] = gpu_state_during(step, torch, args.gpu_state_seconds)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,6 +474,10 @@ def main():
     ap.add_argument("--gpu-state-seconds", type=float, default=1.0,
                     help="length of the pass of back-to-back steps during which the GPU clock and power "
                          "are sampled (0: no such pass, e.g. under a profiler)")
+    ap.add_argument("--sp", type=int, default=1,
+                    help="P > 1: time one rank's share of a P-way sequence-parallel step (its Q shard "
+                         "against the whole gathered K/V; no collectives), for --sp-rank")
+    ap.add_argument("--sp-rank", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the run, copy 256 MiB device to device once: a kernel of known "
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counter readings")
@@ -399,6 +504,11 @@ def main():
         print(json.dumps(res), flush=True)
         return
     cfg = synth.config(args.workload)
+    if args.sp > 1:
+        if args.workload == "quant_long" or args.producer != "none":
+            raise SystemExit("--sp times the attention share: use an attention workload, no --producer")
+        print(json.dumps(run_sp_share(args, torch, synth, sage, cfg)), flush=True)
+        return
     B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
     Np = sage.sage_padded_tokens(N)
     dev = torch.device("cuda:0")

@@ -53,3 +53,19 @@ def test_host_info_fields():
     h = bench.host_info()
     assert set(h) == {"cpu_model", "logical_cpus", "usable_cpus"}
     assert h["usable_cpus"] >= 1 and h["logical_cpus"] >= h["usable_cpus"]
+
+
+def test_sp_shards_cover_the_sequence():
+    """The ranks' token ranges of `--sp P`: contiguous, disjoint, starting on
+    multiples of 64, covering [0, N); ranks past the end hold nothing."""
+    for N, P in ((32760, 8), (4608, 2), (3128, 3), (100, 2), (64, 4)):
+        got = []
+        for r in range(P):
+            a, b = bench.sp_shard(N, P, r)
+            if a >= N:
+                continue
+            assert a % 64 == 0 and a < b <= N
+            got.append((a, b))
+        assert got[0][0] == 0 and got[-1][1] == N
+        assert all(x[1] == y[0] for x, y in zip(got, got[1:]))
+    assert bench.sp_shard(32760, 8, 7) == (28672, 32760)

@@ -474,6 +474,9 @@ def main():
     ap.add_argument("--gpu-state-seconds", type=float, default=1.0,
                     help="length of the pass of back-to-back steps during which the GPU clock and power "
                          "are sampled (0: no such pass, e.g. under a profiler)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step as a HIP graph and replay it for the timed steps (the "
+                         "per-kernel timing pass stays eager)")
     ap.add_argument("--sp", type=int, default=1,
                     help="P > 1: time one rank's share of a P-way sequence-parallel step (its Q shard "
                          "against the whole gathered K/V; no collectives), for --sp-rank")
@@ -609,13 +612,43 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        # one step captured as a HIP graph (fork to the side stream and join
+        # back through events, as in the eager two-stream step), replayed for
+        # the timed steps; the library allocates nothing and issues no memset
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(device=dev)  # default priority
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            cp = int(cap.cuda_stream)
+            side.wait_stream(cap)
+            st = lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
+                                  v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), side_p)
+            st |= qk_call(cp)
+            cap.wait_stream(side)
+            if do_attn:
+                st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
+                                           k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
+                                           v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb,
+                                           kbl, cp)
+        if st != 0:
+            raise RuntimeError(f"libsage call failed with status {st} during capture")
+        stream.wait_stream(cap)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
     # Timed region: exactly K steps, synchronised on both sides.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -683,7 +716,7 @@ def main():
         "data": "synthetic (seeded counter-based normals, bf16 NHD)",
         "config": {"workload": cfg.name, "B": B, "N": N, "H": H, "D": D, "causal": False,
                    "layout": "NHD bf16 in, bf16 out", "seed": args.seed,
-                   "streams": args.streams, "q_block": qb, "k_block": kbl,
+                   "streams": args.streams, "graph": bool(args.graph), "q_block": qb, "k_block": kbl,
                    "producer": prod},
         "kernels_ms": {k2: {"avg": round(avg[k2], 5), "median": round(med[k2], 5),
                             "min": round(mn[k2], 5), "p90": round(p90[k2], 5)} for k2 in per},

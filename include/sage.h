@@ -346,6 +346,7 @@ int sage_gemm_fp8_rowwise(const uint8_t* x8, const float* x_scale, int M, const 
  * (256 queries per workgroup, one per CU) when the grid is at least eight such
  * workgroups per CU deep, else four (128 queries, two per CU: finer load
  * balance for shallow grids).  Without a device a 256-CU part is assumed.
+ * The shape depends on the queries only: for sage_attn_fwd_shard pass N = Nq.
  * Returns SAGE_OK, SAGE_ERR_NULL, or the shape status of sage_attn_fwd. */
 int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
                            int* workgroups);

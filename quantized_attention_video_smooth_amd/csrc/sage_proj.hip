@@ -231,7 +231,27 @@ __global__ __launch_bounds__(GemmCfg::NT, 1) void gemm_fp8_kernel(
     }
     mfmas(af, bf);
   };
+  // The same stage for the steady state, with no conditions: tile t+1 and
+  // tile t+NBUF exist.  Kept free of branches so the compiler's wait counting
+  // sees that this stage's MFMAs need only the fragments read one stage ago
+  // (the explicit wait at its start), not the reads of tile t+1 it has just
+  // issued; with a branch merging in front of the MFMAs it waits for all LDS
+  // reads there, which serialises the next tile's reads with this tile's MFMAs.
+  auto stage_steady = [&](int t, const v8i (&af)[C::TN], const v8i (&bf)[C::TM], v8i (&an)[C::TN],
+                          v8i (&bn)[C::TM]) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(WAIT2);
+    __asm__ volatile("s_barrier" ::: "memory");
+    load_stage(t + C::NBUF);
+    read_frags(t + 1, an, bn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads of tile t+1 ahead of tile t's MFMAs
+    mfmas(af, bf);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   int t = 0;
+  for (; t + C::NBUF + 1 < nk; t += 2) {  // stages t and t+1 both load a tile NBUF ahead
+    stage_steady(t, afA, bfA, afB, bfB);
+    stage_steady(t + 1, afB, bfB, afA, bfA);
+  }
   for (; t + 1 < nk; t += 2) {
     stage(t, afA, bfA, afB, bfB);
     stage(t + 1, afB, bfB, afA, bfA);

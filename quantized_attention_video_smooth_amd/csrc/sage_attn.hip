@@ -331,9 +331,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   // here, in the same basic block as the softmax, so the two can interleave),
   // std::false_type for the last tile.
   // u: t % NBUF (a compile-time constant in the unrolled main loop)
-  auto step = [&](int t, int u, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag, auto next_tag)
-      __attribute__((always_inline)) {
-    const bool issue = t + C::AHEAD < ntiles;
+  // steady_tag: std::true_type when tile t+AHEAD is known to exist, so the
+  // refill and its wait need no run-time condition (no branch merging in
+  // front of the next step's operand reads and their waits).
+  auto step = [&](int t, int u, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag, auto next_tag,
+                  auto steady_tag) __attribute__((always_inline)) {
+    const bool issue = decltype(steady_tag)::value || t + C::AHEAD < ntiles;
     if (issue) gload_lds(t + C::AHEAD, (u + C::AHEAD) % C::NBUF);
     if constexpr (decltype(next_tag)::value) qk_mfma((u + 1) % C::NBUF, snext);
     v8i vop[C::DC];
@@ -364,23 +367,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   const int nfull = Nk / 64;  // tiles without padding keys
   int t = 0;
   // unrolled by the ring depth: the slot of every step is a constant
+  const std::false_type no{};
+  const std::true_type yes{};
+  for (; t + 3 + C::AHEAD < ntiles; t += 4) {  // every step of the group refills the ring
+    step(t, 0, sA, sB, no, yes, yes);
+    step(t + 1, 1, sB, sA, no, yes, yes);
+    step(t + 2, 2, sA, sB, no, yes, yes);
+    step(t + 3, 3, sB, sA, no, yes, yes);
+  }
   for (; t + 4 < ntiles; t += 4) {
-    step(t, 0, sA, sB, std::false_type{}, std::true_type{});
-    step(t + 1, 1, sB, sA, std::false_type{}, std::true_type{});
-    step(t + 2, 2, sA, sB, std::false_type{}, std::true_type{});
-    step(t + 3, 3, sB, sA, std::false_type{}, std::true_type{});
+    step(t, 0, sA, sB, no, yes, no);
+    step(t + 1, 1, sB, sA, no, yes, no);
+    step(t + 2, 2, sA, sB, no, yes, no);
+    step(t + 3, 3, sB, sA, no, yes, no);
   }
   for (; t + 2 < ntiles; t += 2) {
-    step(t, t % C::NBUF, sA, sB, std::false_type{}, std::true_type{});
-    step(t + 1, (t + 1) % C::NBUF, sB, sA, std::false_type{}, std::true_type{});
+    step(t, t % C::NBUF, sA, sB, no, yes, no);
+    step(t + 1, (t + 1) % C::NBUF, sB, sA, no, yes, no);
   }
   auto last_step = [&](int t, v16i (&scur)[2], v16i (&snext)[2]) __attribute__((always_inline)) {
-    if (t < nfull) step(t, t % C::NBUF, scur, snext, std::false_type{}, std::false_type{});
-    else step(t, t % C::NBUF, scur, snext, std::true_type{}, std::false_type{});
+    if (t < nfull) step(t, t % C::NBUF, scur, snext, no, no, no);
+    else step(t, t % C::NBUF, scur, snext, yes, no, no);
   };
   // t is even here: S^T(t) is in sA
   if (t + 1 < ntiles) {
-    step(t, t % C::NBUF, sA, sB, std::false_type{}, std::true_type{});
+    step(t, t % C::NBUF, sA, sB, no, yes, no);
     last_step(t + 1, sB, sA);
   } else {
     last_step(t, sA, sB);

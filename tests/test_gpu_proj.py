@@ -65,9 +65,11 @@ def test_quant_rows_bits(sage, M, K):
 
 
 @pytest.mark.parametrize("M,K,N,with_bias", [(37, 128, 28, True), (300, 384, 260, False),
-                                              (513, 1024, 516, True), (256, 256, 256, True)])
+                                              (513, 1024, 516, True), (256, 256, 256, True),
+                                              (70, 16384, 132, True)])
 def test_gemm_small_full(sage, M, K, N, with_bias):
-    """Ragged M and N (partial 256-blocks on both sides), every entry checked."""
+    """Ragged M and N (partial 256-blocks on both sides), K up to its limit of
+    16384 (256 k-stages), every entry checked."""
     _log(f"[proj] gemm M{M} K{K} N{N} bias {with_bias}")
     x, w, b = synth.proj_inputs(M, K, N, tag=620 + M)
     xc, xs = sage.quant_rows_fp8(x.cuda())

@@ -297,21 +297,18 @@ def run_projection(args, torch, synth, sage):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # timed steps, each call bracketed by events on the stream it runs on
+    evs_all = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs_all[i])
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    per = {"quant_rows_x": [], "gemm": []}
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        step(evs)
-        torch.cuda.synchronize()
-        per["quant_rows_x"].append(evs[0].elapsed_time(evs[1]))
-        per["gemm"].append(evs[1].elapsed_time(evs[2]))
+    per = {"quant_rows_x": [e[0].elapsed_time(e[1]) for e in evs_all],
+           "gemm": [e[1].elapsed_time(e[2]) for e in evs_all]}
     stat = {k: {"avg": round(sum(v) / len(v), 5), "median": round(sorted(v)[len(v) // 2], 5),
                 "min": round(min(v), 5), "p90": round(sorted(v)[min(len(v) - 1, 9 * len(v) // 10)], 5)}
             for k, v in per.items()}
@@ -334,6 +331,7 @@ def run_projection(args, torch, synth, sage):
         "config": {"workload": "vmlp_proj", "M": M, "K": K, "N": N, "seed": args.seed,
                    "weights": "quantised once outside the timed region"},
         "kernels_ms": stat,
+        "kernels_ms_source": "HIP events around each call inside the timed steps",
         "quant_rows_gbs": round(3.0 * M * K / (stat["quant_rows_x"]["avg"] * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "sage_gemm_fp8_rowwise (gemm_fp8_kernel: 256 x 256 blocks, 8 waves)",
                      "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
@@ -403,20 +401,17 @@ def run_sp_share(args, torch, synth, sage, cfg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # timed steps, each call bracketed by events on its stream
+    evs_all = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs_all[i])
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    per = {"quant_q": [], "attn_fwd_shard": []}
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        step(evs)
-        torch.cuda.synchronize()
-        per["quant_q"].append(evs[0].elapsed_time(evs[1]))
-        per["attn_fwd_shard"].append(evs[1].elapsed_time(evs[2]))
+    per = {"quant_q": [e[0].elapsed_time(e[1]) for e in evs_all],
+           "attn_fwd_shard": [e[1].elapsed_time(e[2]) for e in evs_all]}
     stat = {k2: {"avg": round(sum(v2) / len(v2), 5), "median": round(sorted(v2)[len(v2) // 2], 5),
                  "min": round(min(v2), 5), "p90": round(sorted(v2)[min(len(v2) - 1, 9 * len(v2) // 10)], 5)}
             for k2, v2 in per.items()}
@@ -440,6 +435,7 @@ def run_sp_share(args, torch, synth, sage, cfg):
                    "H": H, "D": D, "queries": [a, b], "keys": N, "q_block": qb, "k_block": kbl,
                    "not_in_step": "K/V shard quantisation with all-reduced statistics, K/V all-gather"},
         "kernels_ms": stat,
+        "kernels_ms_source": "HIP events around each call inside the timed steps",
         "roofline": {"kernel": f"sage_attn_fwd_shard (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave "
                                f"workgroups, {wgs} per launch)",
                      "bound": "mfma", "achieved": round(at, 2), "peak": PEAK_MFMA_TFLOPS,
@@ -459,9 +455,10 @@ def main():
                     choices=["tiny", "flux_joint", "video_early", "long_t2v", "quant_long", "vmlp_proj"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--streams", type=int, choices=[1, 2], default=2,
-                    help="2: sage_quant_v runs on a second stream beside sage_quant_qk (they are "
-                         "independent); attention waits for both. 1: all three calls in order")
+    ap.add_argument("--streams", type=int, choices=[1, 2], default=None,
+                    help="2 (default with attention): sage_quant_v runs on a second stream beside "
+                         "sage_quant_qk (they are independent); attention waits for both. 1 (default "
+                         "for quant_long, so each quantiser's event window is its own): in order")
     ap.add_argument("--q-block", type=int, choices=[32, 1], default=32,
                     help="Q scale granularity: one scale per 32-token block (default) or per token")
     ap.add_argument("--k-block", type=int, choices=[64, 16], default=64,
@@ -486,6 +483,8 @@ def main():
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counter readings")
     args = ap.parse_args()
 
+    if args.streams is None:
+        args.streams = 1 if args.workload == "quant_long" else 2
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the path shards over (batch, head) with no "
@@ -570,41 +569,37 @@ def main():
     side_p = int(side.cuda_stream)
     ev_in = [torch.cuda.Event() for _ in range(2)]
 
-    def step_overlapped():
-        # quant_v on the side stream, after the main stream's prior work
-        ev_in[0].record(stream)
-        side.wait_event(ev_in[0])
-        st = lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
-                              v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), side_p)
-        st |= qk_call(sp)
-        ev_in[1].record(side)
-        stream.wait_event(ev_in[1])
-        if do_attn:
-            st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
-                                    k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
-                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, kbl, sp)
-        if st != 0:
-            raise RuntimeError(f"libsage call failed with status {st}")
-
     def step(evs=None):
-        if evs is None and args.streams == 2:
-            step_overlapped()
-            return
-        if evs:
-            evs[0].record(stream)
-        st = qk_call(sp)
-        if evs:
-            evs[1].record(stream)
+        """One step.  evs: {call: (start, end) events} recorded on the stream each
+        call runs on, or None.  With --streams 2, sage_quant_v runs on the side
+        stream beside sage_quant_qk and the attention waits for both."""
+        two = args.streams == 2
+
+        def rec(name, i, s_):
+            if evs:
+                evs[name][i].record(s_)
+
+        st = 0
+        if two:
+            ev_in[0].record(stream)
+            side.wait_event(ev_in[0])
+        vs_, vp_ = (side, side_p) if two else (stream, sp)
+        rec("quant_qk", 0, stream)
+        st |= qk_call(sp)
+        rec("quant_qk", 1, stream)
+        rec("quant_v", 0, vs_)
         st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
-                               v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), sp)
-        if evs:
-            evs[2].record(stream)
+                               v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), vp_)
+        rec("quant_v", 1, vs_)
+        if two:
+            ev_in[1].record(side)
+            stream.wait_event(ev_in[1])
         if do_attn:
+            rec("attn_fwd", 0, stream)
             st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
                                     k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
                                     v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, kbl, sp)
-        if evs:
-            evs[3].record(stream)
+            rec("attn_fwd", 1, stream)
         if st != 0:
             raise RuntimeError(f"libsage call failed with status {st}")
 
@@ -639,29 +634,33 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    # Timed region: exactly K steps, synchronised on both sides.
+    # Timed region: exactly K steps, synchronised on both sides.  Each call is
+    # bracketed by HIP events on the stream it runs on, inside the timed steps.
+    names = ["quant_qk", "quant_v"] + (["attn_fwd"] if do_attn else [])
+    evs_all = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for k2 in names} for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
-            step()
+            step(evs_all[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # Per-kernel durations (separate pass, events between the calls).
-    per = {"quant_qk": [], "quant_v": [], "attn_fwd": []}
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        step(evs)
+    if graph is None:
+        kernels_src = "HIP events around each call inside the timed steps, on the call's stream"
+    else:
+        # a graph replay cannot carry timing events: eager steps after the timed region
+        kernels_src = "HIP events around each call in eager steps after the graph-timed region"
+        for i in range(args.steps):
+            step(evs_all[i])
         torch.cuda.synchronize()
-        per["quant_qk"].append(evs[0].elapsed_time(evs[1]))
-        per["quant_v"].append(evs[1].elapsed_time(evs[2]))
-        per["attn_fwd"].append(evs[2].elapsed_time(evs[3]))
+    per = {k2: [e[k2][0].elapsed_time(e[k2][1]) for e in evs_all] for k2 in names}
     med = {k2: sorted(v2)[len(v2) // 2] for k2, v2 in per.items()}
     avg = {k2: sum(v2) / len(v2) for k2, v2 in per.items()}
     mn = {k2: min(v2) for k2, v2 in per.items()}
@@ -720,6 +719,7 @@ def main():
                    "producer": prod},
         "kernels_ms": {k2: {"avg": round(avg[k2], 5), "median": round(med[k2], 5),
                             "min": round(mn[k2], 5), "p90": round(p90[k2], 5)} for k2 in per},
+        "kernels_ms_source": kernels_src,
         "attn_tflops": round(work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12, 2) if do_attn else None,
         "quant_qk_gbs": round((work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9, 1),
         "quant_v_gbs": round(work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9, 1),

@@ -4,7 +4,7 @@ One step = sage_quant_qk + sage_quant_v + sage_attn_fwd over one batch of
 seeded synthetic bf16 inputs already resident in HBM (default workload: the
 FLUX.3 Action joint block, B2 H24 N4608 D128).  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload flux_joint]
+    python bench.py [--gpus 1] [--steps 30] [--warmup 200] [--workload flux_joint]
 
 `value` is attention TFLOPS over the whole step, 4*B*H*N^2*D / step time (the
 quantisation kernels are inside the step).  Per-kernel times come from HIP
@@ -450,7 +450,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the GPU clock ramps up over the first tens of ms of load "
+                         "(200 FLUX steps are ~0.1 s; 5 leave the timed steps inside the ramp)")
     ap.add_argument("--workload", default="flux_joint",
                     choices=["tiny", "flux_joint", "video_early", "long_t2v", "quant_long", "vmlp_proj"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -206,6 +206,76 @@ class GpuStateSampler:
                 "sclk_mhz": stats(0), "mclk_mhz": stats(1), "socket_power_w": stats(2)}
 
 
+class GraphTimingEvent:
+    """A HIP timing event that a captured graph records on every replay.
+
+    While its stream is being captured, record() adds an event-record node to
+    the capture graph after the stream's current dependencies and makes that
+    node the stream's only dependency, so the node sits between the calls it
+    brackets (hipStreamGetCaptureInfo_v2, hipGraphAddEventRecordNode,
+    hipStreamUpdateCaptureDependencies).  Outside capture it is a plain
+    hipEventRecord.  torch's Event refuses external=True on ROCm, and this HIP
+    rejects hipEventRecordWithFlags(..., hipEventRecordExternal) during capture.
+    Uses the HIP runtime already loaded in the process (torch's, soname
+    libamdhip64.so.7)."""
+
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes as ct
+            hip = ct.CDLL("libamdhip64.so.7")
+            vp, pvp = ct.c_void_p, ct.POINTER(ct.c_void_p)
+            hip.hipEventCreate.argtypes = [pvp]
+            hip.hipEventRecord.argtypes = [vp, vp]
+            hip.hipEventElapsedTime.argtypes = [ct.POINTER(ct.c_float), vp, vp]
+            hip.hipStreamGetCaptureInfo_v2.argtypes = [vp, ct.POINTER(ct.c_int),
+                                                       ct.POINTER(ct.c_ulonglong), pvp,
+                                                       ct.POINTER(pvp), ct.POINTER(ct.c_size_t)]
+            hip.hipGraphAddEventRecordNode.argtypes = [pvp, vp, pvp, ct.c_size_t, vp]
+            hip.hipStreamUpdateCaptureDependencies.argtypes = [vp, pvp, ct.c_size_t, ct.c_uint]
+            cls._hip = hip
+        return cls._hip
+
+    @staticmethod
+    def _check(err, what):
+        if err != 0:
+            raise RuntimeError(f"{what} failed (hipError {err})")
+
+    def __init__(self):
+        import ctypes as ct
+        self._ct = ct
+        self.ev = ct.c_void_p()
+        self._check(self._lib().hipEventCreate(ct.byref(self.ev)), "hipEventCreate")
+
+    def record(self, stream):
+        ct, hip = self._ct, self._lib()
+        sp = ct.c_void_p(int(stream.cuda_stream))
+        status, cid, graph = ct.c_int(), ct.c_ulonglong(), ct.c_void_p()
+        deps, ndeps = ct.POINTER(ct.c_void_p)(), ct.c_size_t()
+        self._check(hip.hipStreamGetCaptureInfo_v2(sp, ct.byref(status), ct.byref(cid), ct.byref(graph),
+                                                   ct.byref(deps), ct.byref(ndeps)),
+                    "hipStreamGetCaptureInfo_v2")
+        if status.value == 0:  # hipStreamCaptureStatusNone
+            self._check(hip.hipEventRecord(self.ev, sp), "hipEventRecord")
+            return
+        if status.value != 1:  # hipStreamCaptureStatusActive
+            raise RuntimeError("stream capture invalidated")
+        dep_list = (ct.c_void_p * max(1, ndeps.value))(*[deps[i] for i in range(ndeps.value)])
+        node = ct.c_void_p()
+        self._check(hip.hipGraphAddEventRecordNode(ct.byref(node), graph, dep_list, ndeps.value, self.ev),
+                    "hipGraphAddEventRecordNode")
+        self._check(hip.hipStreamUpdateCaptureDependencies(sp, ct.byref(node), 1, 1),
+                    "hipStreamUpdateCaptureDependencies")
+
+    def elapsed_time(self, end):
+        ms = self._ct.c_float()
+        self._check(self._lib().hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev),
+                    "hipEventElapsedTime")
+        return float(ms.value)
+
+
 def gpu_state_during(run_step, torch, seconds=1.0):
     """Clock and power while the step runs back to back for `seconds` (a pass
     of its own, after the timed steps)."""
@@ -474,8 +544,9 @@ def main():
                     help="length of the pass of back-to-back steps during which the GPU clock and power "
                          "are sampled (0: no such pass, e.g. under a profiler)")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step as a HIP graph and replay it for the timed steps (the "
-                         "per-kernel timing pass stays eager)")
+                    help="capture the K timed steps as one HIP graph, with timing events around the "
+                         "roofline's call only; after the eager warm-up, replay it once untimed and "
+                         "once timed")
     ap.add_argument("--sp", type=int, default=1,
                     help="P > 1: time one rank's share of a P-way sequence-parallel step (its Q shard "
                          "against the whole gathered K/V; no collectives), for --sp-rank")
@@ -571,37 +642,40 @@ def main():
     side_p = int(side.cuda_stream)
     ev_in = [torch.cuda.Event() for _ in range(2)]
 
-    def step(evs=None):
+    def step(evs=None, main=None):
         """One step.  evs: {call: (start, end) events} recorded on the stream each
         call runs on, or None.  With --streams 2, sage_quant_v runs on the side
-        stream beside sage_quant_qk and the attention waits for both."""
+        stream beside sage_quant_qk and the attention waits for both.  main:
+        the stream of the step (the capture stream under --graph)."""
         two = args.streams == 2
+        stream_ = stream if main is None else main
+        sp_ = int(stream_.cuda_stream)
 
         def rec(name, i, s_):
-            if evs:
+            if evs and name in evs:
                 evs[name][i].record(s_)
 
         st = 0
         if two:
-            ev_in[0].record(stream)
+            ev_in[0].record(stream_)
             side.wait_event(ev_in[0])
-        vs_, vp_ = (side, side_p) if two else (stream, sp)
-        rec("quant_qk", 0, stream)
-        st |= qk_call(sp)
-        rec("quant_qk", 1, stream)
+        vs_, vp_ = (side, side_p) if two else (stream_, sp_)
+        rec("quant_qk", 0, stream_)
+        st |= qk_call(sp_)
+        rec("quant_qk", 1, stream_)
         rec("quant_v", 0, vs_)
         st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
                                v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), vp_)
         rec("quant_v", 1, vs_)
         if two:
             ev_in[1].record(side)
-            stream.wait_event(ev_in[1])
+            stream_.wait_event(ev_in[1])
         if do_attn:
-            rec("attn_fwd", 0, stream)
+            rec("attn_fwd", 0, stream_)
             st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
                                     k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
-                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, kbl, sp)
-            rec("attn_fwd", 1, stream)
+                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, kbl, sp_)
+            rec("attn_fwd", 1, stream_)
         if st != 0:
             raise RuntimeError(f"libsage call failed with status {st}")
 
@@ -609,60 +683,51 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    graph = None
+    names = ["quant_qk", "quant_v"] + (["attn_fwd"] if do_attn else [])
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
     if args.graph:
-        # one step captured as a HIP graph (fork to the side stream and join
-        # back through events, as in the eager two-stream step), replayed for
-        # the timed steps; the library allocates nothing and issues no memset
+        # The K timed steps captured as one HIP graph, the roofline's call
+        # bracketed in each step by timing events that the graph records on
+        # that call's stream.  After the eager warm-up one
+        # untimed replay warms the graph; the timed region is one replay.  The
+        # library allocates nothing and issues no memset, so the graph holds
+        # only the steps' kernels and events.
+        # Only the call the roofline is taken on is bracketed: each event node
+        # costs about as much as replay saves over eager launches.
+        timed = ["attn_fwd"] if do_attn else ["quant_qk"]
+        evs_all = [{k2: (GraphTimingEvent(), GraphTimingEvent()) for k2 in timed}
+                   for _ in range(args.steps)]
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream(device=dev)  # default priority
         cap.wait_stream(stream)
         with torch.cuda.graph(graph, stream=cap):
-            cp = int(cap.cuda_stream)
-            side.wait_stream(cap)
-            st = lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
-                                  v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), side_p)
-            st |= qk_call(cp)
-            cap.wait_stream(side)
-            if do_attn:
-                st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
-                                           k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
-                                           v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb,
-                                           kbl, cp)
-        if st != 0:
-            raise RuntimeError(f"libsage call failed with status {st} during capture")
+            for i in range(args.steps):
+                step(evs_all[i], main=cap)
         stream.wait_stream(cap)
-        for _ in range(args.warmup):
-            graph.replay()
         torch.cuda.synchronize()
-
-    # Timed region: exactly K steps, synchronised on both sides.  Each call is
-    # bracketed by HIP events on the stream it runs on, inside the timed steps.
-    names = ["quant_qk", "quant_v"] + (["attn_fwd"] if do_attn else [])
-    evs_all = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for k2 in names} for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step(evs_all[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-
-    if graph is None:
-        kernels_src = "HIP events around each call inside the timed steps, on the call's stream"
+        graph.replay()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        graph.replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        kernels_src = (f"HIP events around {timed[0]} inside the timed steps (event-record nodes of the "
+                       "replayed graph, on the call's stream)")
     else:
-        # a graph replay cannot carry timing events: eager steps after the timed region
-        kernels_src = "HIP events around each call in eager steps after the graph-timed region"
+        # Each call bracketed by HIP events on the stream it runs on, inside
+        # the timed steps.
+        evs_all = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for k2 in names} for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start.record(stream)
         for i in range(args.steps):
             step(evs_all[i])
+        t_end.record(stream)
         torch.cuda.synchronize()
-    per = {k2: [e[k2][0].elapsed_time(e[k2][1]) for e in evs_all] for k2 in names}
+        kernels_src = "HIP events around each call inside the timed steps, on the call's stream"
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    per = {k2: [e[k2][0].elapsed_time(e[k2][1]) for e in evs_all] for k2 in evs_all[0]}
     med = {k2: sorted(v2)[len(v2) // 2] for k2, v2 in per.items()}
     avg = {k2: sum(v2) / len(v2) for k2, v2 in per.items()}
     mn = {k2: min(v2) for k2, v2 in per.items()}
@@ -723,8 +788,10 @@ def main():
                             "min": round(mn[k2], 5), "p90": round(p90[k2], 5)} for k2 in per},
         "kernels_ms_source": kernels_src,
         "attn_tflops": round(work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12, 2) if do_attn else None,
-        "quant_qk_gbs": round((work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9, 1),
-        "quant_v_gbs": round(work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9, 1),
+        "quant_qk_gbs": (round((work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9, 1)
+                         if "quant_qk" in avg else None),
+        "quant_v_gbs": (round(work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9, 1)
+                        if "quant_v" in avg else None),
         "roofline": roofline,
     }
     if args.gpu_state_seconds > 0:

@@ -1,0 +1,43 @@
+"""bench.py end to end on the tiny workload (B1 H2 N256 D64), eager and with
+--graph: one JSON line with the contract's keys, and per-call times that are
+positive, finite and within the step time.  Under --graph the attention's
+times come from event-record nodes added to the captured graph through the
+HIP graph API, so this also checks that those nodes record on every replay.
+Runs bench.py in a child process (one GPU process at a time)."""
+import json
+import math
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("graph", [False, True], ids=["eager", "graph"])
+def test_bench_tiny(graph):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "5",
+           "--warmup", "3", "--no-cpu-baseline", "--gpu-state-seconds", "0"] + (["--graph"] if graph else [])
+    print("[bench]", " ".join(cmd[1:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = r.stdout.strip().splitlines()[-1]
+    d = json.loads(line)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in d
+    assert d["config"]["graph"] is graph
+    assert d["steps"] == 5 and d["n_gpus"] == 1
+    assert math.isfinite(d["value"]) and d["value"] > 0
+    att = d["kernels_ms"]["attn_fwd"]
+    assert 0 < att["min"] <= att["median"] <= att["p90"]
+    assert att["avg"] <= 5 * d["ms_per_step"]
+    assert 0 < d["roofline"]["frac"] < 1
+    print(f"  step {d['ms_per_step']} ms, attention {att['avg']} ms, kernels {sorted(d['kernels_ms'])}",
+          flush=True)

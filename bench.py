@@ -4,11 +4,20 @@ One step = sage_quant_qk + sage_quant_v + sage_attn_fwd over one batch of
 seeded synthetic bf16 inputs already resident in HBM (default workload: the
 FLUX.3 Action joint block, B2 H24 N4608 D128).  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 200] [--workload flux_joint]
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload flux_joint]
 
 `value` is attention TFLOPS over the whole step, 4*B*H*N^2*D / step time (the
-quantisation kernels are inside the step).  Per-kernel times come from HIP
-events recorded on the stream the kernels run on.
+quantisation kernels are inside the step).  A default run also measures the
+metric's other two parts in the same process and reports them under `parts`:
+attention on the long text-to-video shape (B1 H40 N32760 D128) and the
+quantisers' HBM GB/s on the quant-only shape of the same size.  Each workload
+first runs back-to-back steps for --prewarm-ms (the GPU clock ramps up over
+the first tens of ms of load), then --warmup counted steps.  Per-kernel times
+come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py --workload flux_joint --abba "producer=fused,producer=composed"
+
+compares two step variants in one process, in ABBA groups.
 """
 from __future__ import annotations
 
@@ -364,6 +373,7 @@ def run_projection(args, torch, synth, sage):
         if st != 0:
             raise RuntimeError(f"libsage call failed with status {st}")
 
+    pw = prewarm(step, torch, args.prewarm_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -400,6 +410,7 @@ def run_projection(args, torch, synth, sage):
         "data": "synthetic (seeded counter-based normals: X N(0,1), W N(0,1/K), bias N(0,0.01), bf16)",
         "config": {"workload": "vmlp_proj", "M": M, "K": K, "N": N, "seed": args.seed,
                    "weights": "quantised once outside the timed region"},
+        "prewarm": pw,
         "kernels_ms": stat,
         "kernels_ms_source": "HIP events around each call inside the timed steps",
         "quant_rows_gbs": round(3.0 * M * K / (stat["quant_rows_x"]["avg"] * 1e-3) / 1e9, 1),
@@ -468,6 +479,7 @@ def run_sp_share(args, torch, synth, sage, cfg):
         if st != 0:
             raise RuntimeError(f"libsage call failed with status {st}")
 
+    pw = prewarm(step, torch, args.prewarm_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -504,6 +516,7 @@ def run_sp_share(args, torch, synth, sage, cfg):
         "config": {"workload": f"{cfg.name}, rank {rank} of a {P}-way sequence split", "B": B, "N": N,
                    "H": H, "D": D, "queries": [a, b], "keys": N, "q_block": qb, "k_block": kbl,
                    "not_in_step": "K/V shard quantisation with all-reduced statistics, K/V all-gather"},
+        "prewarm": pw,
         "kernels_ms": stat,
         "kernels_ms_source": "HIP events around each call inside the timed steps",
         "roofline": {"kernel": f"sage_attn_fwd_shard (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave "
@@ -516,15 +529,356 @@ def run_sp_share(args, torch, synth, sage, cfg):
     return res
 
 
+def prewarm(run_step, torch, ms):
+    """Back-to-back steps for at least `ms` of wall time before the counted
+    warm-up: the GPU clock ramps up over the first tens of ms of load, so a
+    short --warmup alone would leave the timed steps inside the ramp."""
+    if ms <= 0:
+        return {"ms": 0.0, "steps": 0}
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            run_step()
+        n += 4
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= ms:
+            return {"ms": round(el, 1), "steps": n}
+
+
+def parse_variant(spec):
+    """'opt=val[;opt=val...]' -> {opt: val} over the step options an ABBA
+    comparison may vary (streams, producer, q_block, k_block)."""
+    allowed = {"streams": int, "producer": str, "q_block": int, "k_block": int}
+    out = {}
+    if spec in ("", "default"):
+        return out
+    for part in spec.split(";"):
+        key, _, val = part.partition("=")
+        key = key.strip().replace("-", "_")
+        if key not in allowed or not val:
+            raise SystemExit(f"--abba: unknown variant option {part!r} (allowed: {sorted(allowed)})")
+        out[key] = allowed[key](val.strip())
+    if out.get("producer", "none") not in ("none", "fused", "composed"):
+        raise SystemExit("--abba: producer is none, fused or composed")
+    if out.get("streams", 1) not in (1, 2) or out.get("q_block", 32) not in (1, 32) \
+            or out.get("k_block", 64) not in (16, 64):
+        raise SystemExit("--abba: streams 1|2, q_block 1|32, k_block 16|64")
+    return out
+
+
+class AttentionPath:
+    """Inputs, outputs and workspaces of one workload, resident in HBM, and the
+    step of the path over them: sage_quant_qk (or the QK producer in front of
+    it) + sage_quant_v + sage_attn_fwd (no attention for quant_long).  Scale
+    buffers are sized for the finest granularities, so one instance serves
+    every step variant."""
+
+    def __init__(self, torch, synth, sage, cfg, seed, need_producer):
+        self.torch, self.sage, self.cfg = torch, sage, cfg
+        self.lib = sage.lib()
+        B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
+        Np = sage.sage_padded_tokens(N)
+        dev = self.dev = torch.device("cuda:0")
+        self.q, self.k, self.v = synth.make_qkv(cfg, seed, device=dev)
+        self.q_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+        self.q_scale = torch.empty((B, H, Np), dtype=torch.float32, device=dev)
+        self.k_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
+        self.k_scale = torch.empty((B, H, Np // 16), dtype=torch.float32, device=dev)
+        self.k_mean = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+        self.v_fp8 = torch.empty((B, H, D, Np), dtype=torch.uint8, device=dev)
+        self.v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        self.v_mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
+        self.ws_qk = torch.empty(max(sage.sage_quant_qk_workspace_size(B, N, H, D),
+                                     sage.sage_norm_rope_quant_qk_workspace_size(B, N, H, D)),
+                                 dtype=torch.uint8, device=dev)
+        self.ws_v = torch.empty(sage.sage_quant_v_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
+        if need_producer:
+            self.wq = synth.norm_weight(cfg, "q").to(dev)
+            self.wk = synth.norm_weight(cfg, "k").to(dev)
+            self.rope = torch.from_numpy(synth.rope_table(N, D)).to(dev)
+            self.yq = torch.empty_like(self.q)
+            self.yk = torch.empty_like(self.k)
+        self.stream = torch.cuda.current_stream()
+        self.side = torch.cuda.Stream(device=dev)  # default priority
+        self.ev_in = [torch.cuda.Event() for _ in range(2)]
+        self.do_attn = cfg.name != "quant_long"
+
+    def step_fn(self, streams, producer, qb, kbl):
+        """The step for these options.  step(evs=None, main=None): evs maps a
+        call name to its (start, end) events, recorded on the stream the call
+        runs on; main is the step's stream (the capture stream under --graph).
+        With streams == 2, sage_quant_v runs on a side stream beside the Q/K
+        segment and the attention waits for both."""
+        lib, cfg = self.lib, self.cfg
+        B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
+        q, k, v, out = self.q, self.k, self.v, self.out
+        qs, ks, vs, os_ = q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3]
+        side, side_p, ev_in = self.side, int(self.side.cuda_stream), self.ev_in
+        eps = 1e-6
+        pq = (self.q_i8.data_ptr(), self.q_scale.data_ptr(), self.k_i8.data_ptr(), self.k_scale.data_ptr(),
+              self.k_mean.data_ptr())
+        pv = (self.v_fp8.data_ptr(), self.v_scale.data_ptr(), self.v_mean.data_ptr())
+        ws_qk, ws_v = self.ws_qk, self.ws_v
+
+        def qk_call(sp_):
+            if producer == "fused":
+                return lib.sage_norm_rope_quant_qk(
+                    q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, self.wq.data_ptr(), self.wk.data_ptr(),
+                    self.rope.data_ptr(), eps, *pq, ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp_)
+            src_q, src_k = q, k
+            st_ = 0
+            if producer == "composed":
+                yq, yk = self.yq, self.yk
+                st_ |= lib.sage_norm_rope(q.data_ptr(), *qs, B, N, H, D, self.wq.data_ptr(),
+                                          self.rope.data_ptr(), eps, yq.data_ptr(), *yq.stride()[:3], sp_)
+                st_ |= lib.sage_norm_rope(k.data_ptr(), *ks, B, N, H, D, self.wk.data_ptr(),
+                                          self.rope.data_ptr(), eps, yk.data_ptr(), *yk.stride()[:3], sp_)
+                src_q, src_k = yq, yk
+            st_ |= lib.sage_quant_qk_ex(src_q.data_ptr(), *src_q.stride()[:3], src_k.data_ptr(),
+                                        *src_k.stride()[:3], B, N, H, D, *pq, ws_qk.data_ptr(),
+                                        ws_qk.numel(), qb, kbl, sp_)
+            return st_
+
+        def step(evs=None, main=None):
+            two = streams == 2
+            stream_ = self.stream if main is None else main
+            sp_ = int(stream_.cuda_stream)
+
+            def rec(name, i, s_):
+                if evs and name in evs:
+                    evs[name][i].record(s_)
+
+            st = 0
+            if two:
+                ev_in[0].record(stream_)
+                side.wait_event(ev_in[0])
+            vs_, vp_ = (side, side_p) if two else (stream_, sp_)
+            rec("quant_qk", 0, stream_)
+            st |= qk_call(sp_)
+            rec("quant_qk", 1, stream_)
+            rec("quant_v", 0, vs_)
+            st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, *pv, ws_v.data_ptr(), ws_v.numel(), vp_)
+            rec("quant_v", 1, vs_)
+            if two:
+                ev_in[1].record(side)
+                stream_.wait_event(ev_in[1])
+            if self.do_attn:
+                rec("attn_fwd", 0, stream_)
+                st |= lib.sage_attn_fwd_ex(pq[0], pq[1], pq[2], pq[3], *pv, B, N, H, D, 0.0,
+                                           out.data_ptr(), *os_, qb, kbl, sp_)
+                rec("attn_fwd", 1, stream_)
+            if st != 0:
+                raise RuntimeError(f"libsage call failed with status {st}")
+
+        return step
+
+
+def _stats(v2):
+    s = sorted(v2)
+    return {"avg": round(sum(v2) / len(v2), 5), "median": round(s[len(s) // 2], 5),
+            "min": round(s[0], 5), "p90": round(s[min(len(s) - 1, (9 * len(s)) // 10)], 5)}
+
+
+def measure_path(args, cfg, torch, synth, sage, streams):
+    """The workload's step: pre-warm, warm-up, K timed steps with per-call HIP
+    events.  Returns the fields of its JSON result (no cpu_baseline)."""
+    B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
+    qb, kbl, prod = args.q_block, args.k_block, args.producer
+    path = AttentionPath(torch, synth, sage, cfg, args.seed, prod != "none")
+    step = path.step_fn(streams, prod, qb, kbl)
+    stream, dev, do_attn = path.stream, path.dev, path.do_attn
+    pw = prewarm(step, torch, args.prewarm_ms)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    names = ["quant_qk", "quant_v"] + (["attn_fwd"] if do_attn else [])
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    if args.graph:
+        # The K timed steps captured as one HIP graph, the roofline's call
+        # bracketed in each step by timing events that the graph records on
+        # that call's stream.  After the eager warm-up one untimed replay warms
+        # the graph; the timed region is one replay.  The library allocates
+        # nothing and issues no memset, so the graph holds only the steps'
+        # kernels and events.  Only the roofline's call is bracketed: each
+        # event node costs about as much as replay saves over eager launches.
+        timed = ["attn_fwd"] if do_attn else ["quant_qk"]
+        evs_all = [{k2: (GraphTimingEvent(), GraphTimingEvent()) for k2 in timed}
+                   for _ in range(args.steps)]
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(device=dev)  # default priority
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.steps):
+                step(evs_all[i], main=cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        graph.replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        kernels_src = (f"HIP events around {timed[0]} inside the timed steps (event-record nodes of the "
+                       "replayed graph, on the call's stream)")
+    else:
+        evs_all = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for k2 in names} for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(evs_all[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        kernels_src = "HIP events around each call inside the timed steps, on the call's stream"
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    per = {k2: [e[k2][0].elapsed_time(e[k2][1]) for e in evs_all] for k2 in evs_all[0]}
+    kstats = {k2: _stats(v2) for k2, v2 in per.items()}
+    avg = {k2: s["avg"] for k2, s in kstats.items()}
+
+    work = algorithmic(B, N, H, D, qb, kbl)
+    if prod != "none":
+        # the rotation table, read once per step (the weights are negligible);
+        # the Q/K segment's bytes are otherwise those of the quantiser
+        work["quant_q_bytes"] += 4.0 * N * D
+    step_s = ms_per_step * 1e-3
+    res = {"ms_per_step": round(ms_per_step, 5), "prewarm": pw}
+    if do_attn:
+        waves, wgs = sage.sage_attn_launch_shape(B, N, H, D)
+        attn_tflops = work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12
+        res["value"] = round(work["attn_ops"] / step_s / 1e12, 3)
+        res["unit"] = "TFLOPS"
+        res["roofline"] = {
+            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave workgroups, "
+                      f"{wgs} per launch)",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
+            "traffic": traffic_record(os.path.join(ROOT, "quantized_attention_video_smooth_amd",
+                                                   "csrc", "sage_attn.hip"), cfg.name, qb, kbl),
+        }
+        res["attn_tflops"] = round(attn_tflops, 2)
+    else:
+        qv_bytes = work["quant_q_bytes"] + work["quant_k_bytes"] + work["quant_v_bytes"]
+        res["value"] = round(qv_bytes / step_s / 1e9, 3)
+        res["unit"] = "GB/s"
+        gbs = (work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9
+        gbs_v = work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9
+        src = os.path.join(ROOT, "quantized_attention_video_smooth_amd", "csrc", "sage_quant.hip")
+        res["roofline"] = {"kernel": "sage_quant_qk (its statistics, finalisation and quantisation "
+                                     "kernels, one call)",
+                           "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 4),
+                           "traffic": traffic_record(src, cfg.name, qb, kbl, kernel="quant_qk")}
+        res["roofline_quant_v"] = {"kernel": "sage_quant_v (its statistics, finalisation and quantisation "
+                                             "kernels, one call)",
+                                   "bound": "hbm", "achieved": round(gbs_v, 1), "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": round(gbs_v / PEAK_HBM_GBS, 4),
+                                   "traffic": traffic_record(src, cfg.name, qb, kbl, kernel="quant_v")}
+        res["quant_qk_gbs"] = round(gbs, 1)
+        res["quant_v_gbs"] = round(gbs_v, 1)
+    res["config"] = {"workload": cfg.name, "B": B, "N": N, "H": H, "D": D, "causal": False,
+                     "layout": "NHD bf16 in, bf16 out", "seed": args.seed,
+                     "streams": streams, "graph": bool(args.graph), "q_block": qb, "k_block": kbl,
+                     "producer": prod}
+    res["kernels_ms"] = kstats
+    res["kernels_ms_source"] = kernels_src
+    res["_step"] = step
+    return res
+
+
+def run_abba(args, cfg, torch, synth, sage):
+    """Same-process ABBA comparison of two step variants on one workload (the
+    pages' protocol for their last gains): every group times K steps of A, K
+    of B, K of B, K of A, each block bracketed by events; a group gives the
+    mean step time of each variant and their ratio B/A."""
+    specs = args.abba.split(",")
+    if len(specs) != 2:
+        raise SystemExit("--abba takes two variants: A,B (each 'opt=val[;opt=val]' or 'default')")
+    base = {"streams": args.streams, "producer": args.producer, "q_block": args.q_block,
+            "k_block": args.k_block}
+    var = []
+    for s in specs:
+        o = dict(base)
+        o.update(parse_variant(s))
+        var.append(o)
+    need_prod = any(o["producer"] != "none" for o in var)
+    path = AttentionPath(torch, synth, sage, cfg, args.seed, need_prod)
+    steps = [path.step_fn(o["streams"], o["producer"], o["q_block"], o["k_block"]) for o in var]
+    key = "attn_fwd" if path.do_attn else "quant_qk"
+
+    def block(step):
+        evs = [{key: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))}
+               for _ in range(args.steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(path.stream)
+        for i in range(args.steps):
+            step(evs[i])
+        t1.record(path.stream)
+        torch.cuda.synchronize()
+        call = [e[key][0].elapsed_time(e[key][1]) for e in evs]
+        return t0.elapsed_time(t1) / args.steps, sum(call) / len(call)
+
+    pw = prewarm(lambda: (steps[0](), steps[1]()), torch, args.prewarm_ms)
+    for _ in range(args.warmup):
+        steps[0]()
+        steps[1]()
+    torch.cuda.synchronize()
+    groups = []
+    for _ in range(args.abba_groups):
+        a1, b1, b2, a2 = block(steps[0]), block(steps[1]), block(steps[1]), block(steps[0])
+        ga = ((a1[0] + a2[0]) / 2, (a1[1] + a2[1]) / 2)
+        gb = ((b1[0] + b2[0]) / 2, (b1[1] + b2[1]) / 2)
+        groups.append({"A_step_ms": round(ga[0], 5), "B_step_ms": round(gb[0], 5),
+                       f"A_{key}_ms": round(ga[1], 5), f"B_{key}_ms": round(gb[1], 5),
+                       "ratio_step": round(gb[0] / ga[0], 5), f"ratio_{key}": round(gb[1] / ga[1], 5)})
+
+    def med(xs):
+        s = sorted(xs)
+        return s[len(s) // 2]
+
+    return {
+        "mode": "abba",
+        "workload": cfg.name,
+        "A": var[0], "B": var[1],
+        "groups": args.abba_groups, "steps_per_block": args.steps, "warmup": args.warmup, "prewarm": pw,
+        "median_A_step_ms": med([g["A_step_ms"] for g in groups]),
+        "median_B_step_ms": med([g["B_step_ms"] for g in groups]),
+        f"median_A_{key}_ms": med([g[f"A_{key}_ms"] for g in groups]),
+        f"median_B_{key}_ms": med([g[f"B_{key}_ms"] for g in groups]),
+        "median_ratio_step": med([g["ratio_step"] for g in groups]),
+        f"median_ratio_{key}": med([g[f"ratio_{key}"] for g in groups]),
+        "ratio_step_range": [min(g["ratio_step"] for g in groups), max(g["ratio_step"] for g in groups)],
+        "per_group": groups,
+    }
+
+
+# The metric's other parts, measured after the main workload in a default run
+# (attention at N = 32760, quantiser GB/s on the quant-only shape).
+DEFAULT_PARTS = ("long_t2v", "quant_long")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first: the GPU clock ramps up over the first tens of ms of load "
-                         "(200 FLUX steps are ~0.1 s; 5 leave the timed steps inside the ramp)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="back-to-back untimed steps for at least this many ms before the counted "
+                         "warm-up of each workload (the GPU clock ramps up over the first tens of ms "
+                         "of load); reported as 'prewarm'")
     ap.add_argument("--workload", default="flux_joint",
                     choices=["tiny", "flux_joint", "video_early", "long_t2v", "quant_long", "vmlp_proj"])
+    ap.add_argument("--parts", default=None,
+                    help="comma-separated further workloads measured in the same run and reported under "
+                         "'parts' (default: long_t2v,quant_long when the workload is flux_joint, none "
+                         "otherwise; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--streams", type=int, choices=[1, 2], default=None,
@@ -551,18 +905,29 @@ def main():
                     help="P > 1: time one rank's share of a P-way sequence-parallel step (its Q shard "
                          "against the whole gathered K/V; no collectives), for --sp-rank")
     ap.add_argument("--sp-rank", type=int, default=0)
+    ap.add_argument("--abba", default=None,
+                    help="A,B: same-process ABBA comparison of two step variants on --workload, each "
+                         "'opt=val[;opt=val]' over streams, producer, q_block, k_block (or 'default'); "
+                         "--steps steps per block, --abba-groups groups")
+    ap.add_argument("--abba-groups", type=int, default=15)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the run, copy 256 MiB device to device once: a kernel of known "
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counter readings")
     args = ap.parse_args()
 
-    if args.streams is None:
-        args.streams = 1 if args.workload == "quant_long" else 2
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the path shards over (batch, head) with no "
               "exchange, and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.parts is None:
+        parts = list(DEFAULT_PARTS) if (args.workload == "flux_joint" and args.sp == 1 and not args.abba
+                                        and args.producer == "none") else []
+    else:
+        parts = [p for p in args.parts.split(",") if p and p != "none"]
+    for p in parts:
+        if p not in ("tiny", "flux_joint", "video_early", "long_t2v", "quant_long"):
+            raise SystemExit(f"--parts: unknown workload {p!r}")
 
     import torch
     import synth
@@ -571,7 +936,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    lib = sage.lib()
+    sage.lib()
     if args.workload == "vmlp_proj":
         res = run_projection(args, torch, synth, sage)
         if args.copy_calibration:
@@ -584,222 +949,45 @@ def main():
             raise SystemExit("--sp times the attention share: use an attention workload, no --producer")
         print(json.dumps(run_sp_share(args, torch, synth, sage, cfg)), flush=True)
         return
-    B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
-    Np = sage.sage_padded_tokens(N)
-    dev = torch.device("cuda:0")
-    q, k, v = synth.make_qkv(cfg, args.seed, device=dev)
-    q_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
-    qb = args.q_block
-    q_scale = torch.empty((B, H, Np // qb), dtype=torch.float32, device=dev)
-    k_i8 = torch.empty((B, H, Np, D), dtype=torch.int8, device=dev)
-    kbl = args.k_block
-    k_scale = torch.empty((B, H, Np // kbl), dtype=torch.float32, device=dev)
-    k_mean = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
-    v_fp8 = torch.empty((B, H, D, Np), dtype=torch.uint8, device=dev)
-    v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    v_mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
-    ws_qk = torch.empty(max(sage.sage_quant_qk_workspace_size(B, N, H, D),
-                            sage.sage_norm_rope_quant_qk_workspace_size(B, N, H, D)),
-                        dtype=torch.uint8, device=dev)
-    ws_v = torch.empty(sage.sage_quant_v_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-    sp = int(stream.cuda_stream)
-    qs, ks, vs, os_ = q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3]
-    do_attn = args.workload != "quant_long"
-    prod = args.producer
-    if prod != "none":
-        wq = synth.norm_weight(cfg, "q").to(dev)
-        wk = synth.norm_weight(cfg, "k").to(dev)
-        rope = torch.from_numpy(synth.rope_table(N, D)).to(dev)
-        yq = torch.empty_like(q)
-        yk = torch.empty_like(k)
-        eps = 1e-6
+    if args.streams is None:
+        args.streams = 1 if args.workload == "quant_long" else 2
+    if args.abba:
+        print(json.dumps(run_abba(args, cfg, torch, synth, sage)), flush=True)
+        return
 
-    def qk_call(sp_):
-        """The Q/K segment of a step: the quantiser, with the producer in front
-        of it when --producer is given."""
-        if prod == "fused":
-            return lib.sage_norm_rope_quant_qk(
-                q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, wq.data_ptr(), wk.data_ptr(),
-                rope.data_ptr(), eps, q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
-                k_scale.data_ptr(), k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp_)
-        src_q, src_k = q, k
-        st_ = 0
-        if prod == "composed":
-            st_ |= lib.sage_norm_rope(q.data_ptr(), *qs, B, N, H, D, wq.data_ptr(), rope.data_ptr(),
-                                      eps, yq.data_ptr(), *yq.stride()[:3], sp_)
-            st_ |= lib.sage_norm_rope(k.data_ptr(), *ks, B, N, H, D, wk.data_ptr(), rope.data_ptr(),
-                                      eps, yk.data_ptr(), *yk.stride()[:3], sp_)
-            src_q, src_k = yq, yk
-        st_ |= lib.sage_quant_qk_ex(src_q.data_ptr(), *src_q.stride()[:3], src_k.data_ptr(),
-                                    *src_k.stride()[:3], B, N, H, D, q_i8.data_ptr(),
-                                    q_scale.data_ptr(), k_i8.data_ptr(), k_scale.data_ptr(),
-                                    k_mean.data_ptr(), ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp_)
-        return st_
-
-    side = torch.cuda.Stream(device=dev)  # default priority
-    side_p = int(side.cuda_stream)
-    ev_in = [torch.cuda.Event() for _ in range(2)]
-
-    def step(evs=None, main=None):
-        """One step.  evs: {call: (start, end) events} recorded on the stream each
-        call runs on, or None.  With --streams 2, sage_quant_v runs on the side
-        stream beside sage_quant_qk and the attention waits for both.  main:
-        the stream of the step (the capture stream under --graph)."""
-        two = args.streams == 2
-        stream_ = stream if main is None else main
-        sp_ = int(stream_.cuda_stream)
-
-        def rec(name, i, s_):
-            if evs and name in evs:
-                evs[name][i].record(s_)
-
-        st = 0
-        if two:
-            ev_in[0].record(stream_)
-            side.wait_event(ev_in[0])
-        vs_, vp_ = (side, side_p) if two else (stream_, sp_)
-        rec("quant_qk", 0, stream_)
-        st |= qk_call(sp_)
-        rec("quant_qk", 1, stream_)
-        rec("quant_v", 0, vs_)
-        st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, v_fp8.data_ptr(), v_scale.data_ptr(),
-                               v_mean.data_ptr(), ws_v.data_ptr(), ws_v.numel(), vp_)
-        rec("quant_v", 1, vs_)
-        if two:
-            ev_in[1].record(side)
-            stream_.wait_event(ev_in[1])
-        if do_attn:
-            rec("attn_fwd", 0, stream_)
-            st |= lib.sage_attn_fwd_ex(q_i8.data_ptr(), q_scale.data_ptr(), k_i8.data_ptr(),
-                                    k_scale.data_ptr(), v_fp8.data_ptr(), v_scale.data_ptr(),
-                                    v_mean.data_ptr(), B, N, H, D, 0.0, out.data_ptr(), *os_, qb, kbl, sp_)
-            rec("attn_fwd", 1, stream_)
-        if st != 0:
-            raise RuntimeError(f"libsage call failed with status {st}")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    names = ["quant_qk", "quant_v"] + (["attn_fwd"] if do_attn else [])
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    if args.graph:
-        # The K timed steps captured as one HIP graph, the roofline's call
-        # bracketed in each step by timing events that the graph records on
-        # that call's stream.  After the eager warm-up one
-        # untimed replay warms the graph; the timed region is one replay.  The
-        # library allocates nothing and issues no memset, so the graph holds
-        # only the steps' kernels and events.
-        # Only the call the roofline is taken on is bracketed: each event node
-        # costs about as much as replay saves over eager launches.
-        timed = ["attn_fwd"] if do_attn else ["quant_qk"]
-        evs_all = [{k2: (GraphTimingEvent(), GraphTimingEvent()) for k2 in timed}
-                   for _ in range(args.steps)]
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream(device=dev)  # default priority
-        cap.wait_stream(stream)
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(args.steps):
-                step(evs_all[i], main=cap)
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        graph.replay()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        kernels_src = (f"HIP events around {timed[0]} inside the timed steps (event-record nodes of the "
-                       "replayed graph, on the call's stream)")
-    else:
-        # Each call bracketed by HIP events on the stream it runs on, inside
-        # the timed steps.
-        evs_all = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    for k2 in names} for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for i in range(args.steps):
-            step(evs_all[i])
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        kernels_src = "HIP events around each call inside the timed steps, on the call's stream"
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    per = {k2: [e[k2][0].elapsed_time(e[k2][1]) for e in evs_all] for k2 in evs_all[0]}
-    med = {k2: sorted(v2)[len(v2) // 2] for k2, v2 in per.items()}
-    avg = {k2: sum(v2) / len(v2) for k2, v2 in per.items()}
-    mn = {k2: min(v2) for k2, v2 in per.items()}
-    p90 = {k2: sorted(v2)[min(len(v2) - 1, (9 * len(v2)) // 10)] for k2, v2 in per.items()}
-
-    work = algorithmic(B, N, H, D, qb, kbl)
-    if prod != "none":
-        # the rotation table, read once per step (the weights are negligible);
-        # the Q/K segment's bytes are otherwise those of the quantiser
-        work["quant_q_bytes"] += 4.0 * N * D
-    waves, wgs = sage.sage_attn_launch_shape(B, N, H, D)
-    step_s = ms_per_step * 1e-3
-    if do_attn:
-        value = work["attn_ops"] / step_s / 1e12
-        attn_tflops = work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12
-        roofline = {
-            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave workgroups, "
-                      f"{wgs} per launch)",
-            "bound": "mfma",
-            "achieved": round(attn_tflops, 2),
-            "peak": PEAK_MFMA_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
-            "traffic": traffic_record(os.path.join(ROOT, "quantized_attention_video_smooth_amd",
-                                                   "csrc", "sage_attn.hip"), cfg.name, qb, kbl),
-        }
-        unit = "TFLOPS"
-    else:
-        qv_bytes = work["quant_q_bytes"] + work["quant_k_bytes"] + work["quant_v_bytes"]
-        value = qv_bytes / step_s / 1e9
-        gbs = (work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9
-        roofline = {"kernel": "sage_quant_qk (stats_kernel, finalize_kernel, qk_quant_kernel)",
-                    "bound": "hbm", "achieved": round(gbs, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                    "traffic": traffic_record(os.path.join(ROOT, "quantized_attention_video_smooth_amd",
-                                                           "csrc", "sage_quant.hip"), cfg.name, qb, kbl,
-                                              kernel="quant_qk")}
-        unit = "GB/s"
-
+    main_res = measure_path(args, cfg, torch, synth, sage, args.streams)
+    step = main_res.pop("_step")
     res = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": unit,
+        "value": main_res.pop("value"),
+        "unit": main_res.pop("unit"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": main_res.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 QK / fp8-e4m3 PV, fp32 softmax+accum",
         "data": "synthetic (seeded counter-based normals, bf16 NHD)",
-        "config": {"workload": cfg.name, "B": B, "N": N, "H": H, "D": D, "causal": False,
-                   "layout": "NHD bf16 in, bf16 out", "seed": args.seed,
-                   "streams": args.streams, "graph": bool(args.graph), "q_block": qb, "k_block": kbl,
-                   "producer": prod},
-        "kernels_ms": {k2: {"avg": round(avg[k2], 5), "median": round(med[k2], 5),
-                            "min": round(mn[k2], 5), "p90": round(p90[k2], 5)} for k2 in per},
-        "kernels_ms_source": kernels_src,
-        "attn_tflops": round(work["attn_ops"] / (avg["attn_fwd"] * 1e-3) / 1e12, 2) if do_attn else None,
-        "quant_qk_gbs": (round((work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9, 1)
-                         if "quant_qk" in avg else None),
-        "quant_v_gbs": (round(work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9, 1)
-                        if "quant_v" in avg else None),
-        "roofline": roofline,
     }
+    res.update(main_res)
     if args.gpu_state_seconds > 0:
         res["gpu_state"] = gpu_state_during(step, torch, args.gpu_state_seconds)
+    del step
+    if parts:
+        res["parts"] = {}
+        for p in parts:
+            pcfg = synth.config(p)
+            pres = measure_path(args, pcfg, torch, synth, sage, 1 if p == "quant_long" else args.streams)
+            pres.pop("_step")
+            pres["steps"], pres["warmup"] = args.steps, args.warmup
+            res["parts"][p] = pres
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
     if args.copy_calibration:
-        copy_calibration(torch, dev)
+        copy_calibration(torch, torch.device("cuda:0"))
     print(json.dumps(res), flush=True)
 
 

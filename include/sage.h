@@ -5,8 +5,9 @@
  *
  * Source pages (cited by title and section):
  *   "FLUX.3 Action RTX 5090 report", §02 Engineering: stage 03 "SageAttention2"
- *     (per-block INT8 QK, FP8 PV, FP32 accumulation, K smooth and V smooth kept,
- *     NHD layout); stage 04 (fusions bit-exact against the unfused path);
+ *     (INT8 QK with per-thread scales, FP8 PV, FP32 accumulation, K smooth and
+ *     V smooth kept, NHD layout; the scales here are per block of 32 Q / 64 K
+ *     tokens, a reading of "per-thread" for the MFMA tiles of this chip); stage 04 (fusions bit-exact against the unfused path);
  *     card A (K centring fused into the INT8 quantiser, BF16 rounding kept);
  *     card B (producers write BF16 NHD directly); card C (V read as a slice of
  *     the V+MLP projection; tiled transpose, padding and permutation).

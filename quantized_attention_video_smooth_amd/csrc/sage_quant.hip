@@ -1,8 +1,9 @@
 // Quantisation kernels of libsage (gfx950): K smoothing + INT8 K, INT8 Q,
 // V smoothing + FP8 E4M3 V with transpose, zero padding and token permutation.
 //
-// Method: "FLUX.3 Action RTX 5090 report", §02 stage 03 (per-block INT8 QK,
-// FP8 PV, K and V smoothing) and card A (the K centring is done inside the
+// Method: "FLUX.3 Action RTX 5090 report", §02 stage 03 (INT8 QK with
+// per-thread scales, read here as per block of 32 Q / 64 K tokens; FP8 PV; K
+// and V smoothing) and card A (the K centring is done inside the
 // quantiser, keeping the BF16 rounding of K - mean); card C (V is transposed,
 // padded and permuted in one tiled pass; its mean, scale and quantisation are
 // kept).  E4M3 layout per "Why can an A10 run FLUX.1", §1.1.

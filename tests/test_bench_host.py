@@ -69,3 +69,13 @@ def test_sp_shards_cover_the_sequence():
         assert got[0][0] == 0 and got[-1][1] == N
         assert all(x[1] == y[0] for x, y in zip(got, got[1:]))
     assert bench.sp_shard(32760, 8, 7) == (28672, 32760)
+
+
+def test_abba_variant_parsing():
+    assert bench.parse_variant("default") == {}
+    assert bench.parse_variant("producer=fused;streams=1") == {"producer": "fused", "streams": 1}
+    assert bench.parse_variant("q-block=1;k_block=16") == {"q_block": 1, "k_block": 16}
+    import pytest
+    for bad in ("waves=3", "producer=both", "streams=3", "k_block=32", "q_block"):
+        with pytest.raises(SystemExit):
+            bench.parse_variant(bad)

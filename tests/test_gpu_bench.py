@@ -41,3 +41,40 @@ def test_bench_tiny(graph):
     assert 0 < d["roofline"]["frac"] < 1
     print(f"  step {d['ms_per_step']} ms, attention {att['avg']} ms, kernels {sorted(d['kernels_ms'])}",
           flush=True)
+
+
+def _run_bench(args):
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py")] + args
+    print("[bench]", " ".join(cmd[1:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def test_bench_parts():
+    """The metric's other parts in the same JSON line: an attention part and a
+    quant-only part, each with its own roofline and pre-warm record."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    d = _run_bench(["--workload", "tiny", "--parts", "tiny,quant_long", "--steps", "3", "--warmup", "1",
+                    "--prewarm-ms", "20", "--no-cpu-baseline", "--gpu-state-seconds", "0"])
+    assert d["prewarm"]["steps"] >= 4
+    assert set(d["parts"]) == {"tiny", "quant_long"}
+    pa, pq = d["parts"]["tiny"], d["parts"]["quant_long"]
+    assert pa["unit"] == "TFLOPS" and 0 < pa["roofline"]["frac"] < 1 and pa["roofline"]["bound"] == "mfma"
+    assert pq["unit"] == "GB/s" and pq["roofline"]["bound"] == "hbm" and pq["config"]["streams"] == 1
+    assert 0 < pq["roofline"]["frac"] < 1 and 0 < pq["roofline_quant_v"]["frac"] < 1
+    print(f"  parts: tiny {pa['ms_per_step']} ms, quant_long {pq['quant_qk_gbs']} / {pq['quant_v_gbs']} GB/s",
+          flush=True)
+
+
+def test_bench_abba():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    d = _run_bench(["--workload", "tiny", "--abba", "streams=1,streams=2", "--abba-groups", "3", "--steps", "3",
+                    "--warmup", "1", "--prewarm-ms", "20"])
+    assert d["mode"] == "abba" and d["A"]["streams"] == 1 and d["B"]["streams"] == 2
+    assert len(d["per_group"]) == 3
+    assert all(g["A_step_ms"] > 0 and g["B_step_ms"] > 0 for g in d["per_group"])
+    assert d["median_ratio_step"] > 0
+    print(f"  ABBA streams 1 vs 2 on tiny: step ratio {d['median_ratio_step']}", flush=True)

@@ -2,10 +2,11 @@
 
 Bar: bit-exact INT8 Q/K codes, FP8 V codes, all scales and means (padding
 included); attention within relative L2 <= 5e-3 of the oracle's quantised
-tiled path and <= 3e-2 of exact fp64 attention.  On the tiny workload the
-method itself is ~3.6e-2 from exact attention (FP8 rounding of P and V), so
-there the second bar is checked as "no worse than the oracle by more than
-5e-3" and the conflict is recorded.
+tiled path (also per (b, h), on the attention term O - v_mean, and with a
+max-abs guard: tests/attn_bars.py) and <= 3e-2 of exact fp64 attention.  On
+the tiny workload the method itself is ~3.6e-2 from exact attention (FP8
+rounding of P and V), so there the exact-attention bar is a strict xfail: the
+conflict shows in the results instead of passing.
 """
 import hashlib
 import math
@@ -17,6 +18,7 @@ import torch
 
 import oracle
 import synth
+from tests.attn_bars import check_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +71,21 @@ def _rows_gathered(out_nhd, rows):
     return out_nhd.float().cpu()[:, rows].permute(0, 2, 1, 3).double().numpy()
 
 
+def _tiled_by_heads(ref_qk, ref_v, rows, cfg, group=8):
+    """The oracle's tiled attention, a group of heads per call (with a progress
+    line per group: the long workload takes minutes on the host)."""
+    parts = []
+    for h0 in range(0, cfg.H, group):
+        sl = slice(h0, min(cfg.H, h0 + group))
+        sub_qk = {k2: (v2[:, sl] if isinstance(v2, np.ndarray) and v2.ndim >= 3 else v2)
+                  for k2, v2 in ref_qk.items()}
+        sub_v = {k2: (v2[:, sl] if isinstance(v2, np.ndarray) and v2.ndim >= 3 else v2)
+                 for k2, v2 in ref_v.items()}
+        parts.append(oracle.attn_tiled(sub_qk, sub_v, rows=rows))
+        _log(f"  oracle heads {sl.start}..{sl.stop - 1} done")
+    return np.concatenate(parts, axis=1)
+
+
 SMALL = [
     synth.config(0),
     synth.custom(1, 1, 2, 64, tag=301),
@@ -97,10 +114,25 @@ def test_small_shapes_full(sage, cfg):
     exact = oracle.attn_exact(q, k, v)
     e_or, e_ex, e_me = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact), oracle.rel_l2(tiled, exact)
     _log(f"  rel L2: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}  oracle-vs-exact {e_me:.3e}")
-    assert e_or <= TOL_ORACLE
+    check_attention(got, tiled, vq[2].cpu().numpy(), log=_log)
     if cfg.N == 1:
         np.testing.assert_array_equal(got, exact.astype(np.float32).astype(np.float64))
-    assert e_ex <= max(TOL_EXACT, e_me + TOL_ORACLE)
+    if cfg.name != "tiny":
+        assert e_ex <= TOL_EXACT
+
+
+@pytest.mark.xfail(strict=True, reason="method conflict: on the tiny workload (no V mean offset, N=256) "
+                   "E4M3 rounding of both P and V puts the method itself ~3.6e-2 from exact fp64 "
+                   "attention, above the 3e-2 bar; the oracle's quantised path is as far")
+def test_tiny_exact_bar(sage):
+    cfg = synth.config(0)
+    q, k, v = synth.make_qkv(cfg)
+    _, _, _, qk, vq = _gpu_quant(sage, q, k, v)
+    out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
+    torch.cuda.synchronize()
+    e_ex = oracle.rel_l2(_rows_gathered(out, np.arange(cfg.N)), oracle.attn_exact(q, k, v))
+    _log(f"[parity] tiny gpu-vs-exact {e_ex:.3e} (bar {TOL_EXACT})")
+    assert e_ex <= TOL_EXACT
 
 
 WORKLOADS = [1, 2]
@@ -117,15 +149,18 @@ def test_workload_quant_bits_and_attention(sage, idx):
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
     out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
     torch.cuda.synchronize()
-    rows = synth.query_subset(cfg.N, every=16)
-    got = _rows_gathered(out, rows)
-    tiled = oracle.attn_tiled(ref_qk, ref_v, rows=rows)
-    exact = oracle.attn_exact(q, k, v, rows=rows)
-    e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
-    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}  "
-         f"oracle-vs-exact {oracle.rel_l2(tiled, exact):.3e}")
-    assert e_or <= TOL_ORACLE and e_ex <= TOL_EXACT
     assert torch.isfinite(out.float()).all()
+    # every query row against the oracle's tiled path
+    got = _rows_gathered(out, np.arange(cfg.N))
+    tiled = _tiled_by_heads(ref_qk, ref_v, None, cfg)
+    check_attention(got, tiled, ref_v["v_mean"], log=_log, label=f"all {cfg.N} rows ")
+    # every 8th 32-query block plus the last against exact fp64 attention
+    rows = synth.query_subset(cfg.N, every=8)
+    exact = oracle.attn_exact(q, k, v, rows=rows)
+    e_ex = oracle.rel_l2(_rows_gathered(out, rows), exact)
+    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-exact {e_ex:.3e}  "
+         f"oracle-vs-exact {oracle.rel_l2(tiled[:, :, rows], exact):.3e}")
+    assert e_ex <= TOL_EXACT
 
 
 def test_long_workload_sampled(sage):
@@ -140,15 +175,20 @@ def test_long_workload_sampled(sage):
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
     out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
     torch.cuda.synchronize()
-    nb = math.ceil(cfg.N / 32)
-    blocks = [0, nb // 3, (2 * nb) // 3, nb - 1]
-    rows = np.array([r for b in blocks for r in range(32 * b, min(cfg.N, 32 * b + 32))], np.int32)
+    assert torch.isfinite(out.float()).all()
+    # the stratified subset: every 8th 32-query block of every head plus the last
+    rows = synth.query_subset(cfg.N, every=8)
     got = _rows_gathered(out, rows)
-    tiled = oracle.attn_tiled(ref_qk, ref_v, rows=rows)
-    exact = oracle.attn_exact(q, k, v, rows=rows)
-    e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
-    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}")
-    assert e_or <= TOL_ORACLE and e_ex <= TOL_EXACT
+    tiled = _tiled_by_heads(ref_qk, ref_v, rows, cfg)
+    check_attention(got, tiled, ref_v["v_mean"], log=_log, label=f"rows {rows.size}/{cfg.N} ")
+    # exact fp64 attention on every 64th block plus the last
+    rows_x = synth.query_subset(cfg.N, every=64)
+    exact = oracle.attn_exact(q, k, v, rows=rows_x)
+    sel = np.searchsorted(rows, rows_x)
+    assert np.array_equal(rows[sel], rows_x)
+    e_ex = oracle.rel_l2(got[:, :, sel], exact)
+    _log(f"  rows {rows_x.size}/{cfg.N}: gpu-vs-exact {e_ex:.3e}")
+    assert e_ex <= TOL_EXACT
 
 
 def test_quant_long_bits(sage):
@@ -216,7 +256,7 @@ def test_sm_scale_argument(sage):
     out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N, sm_scale=0.05)
     torch.cuda.synchronize()
     got = _rows_gathered(out, np.arange(cfg.N))
-    assert oracle.rel_l2(got, oracle.attn_tiled(ref_qk, ref_v, sm_scale=0.05)) <= TOL_ORACLE
+    check_attention(got, oracle.attn_tiled(ref_qk, ref_v, sm_scale=0.05), ref_v["v_mean"], log=_log)
 
 
 def test_errors_enqueue_nothing(sage):
@@ -267,7 +307,7 @@ def test_degenerate_inputs(sage, D, k_block):
     torch.cuda.synchronize()
     got = _rows_gathered(out, np.arange(cfg.N))
     tiled = oracle.attn_tiled(ref_qk, ref_v)
-    assert oracle.rel_l2(got, tiled) <= TOL_ORACLE
+    check_attention(got, tiled, ref_v["v_mean"], log=_log)
     # the constant channel comes back as bf16(v_mean) in every row
     vm = torch.tensor(ref_v["v_mean"][:, 1, 7]).to(torch.bfloat16)
     col = out[:, :, 1, 7].cpu()
@@ -316,14 +356,15 @@ def test_granularity_full(sage, cfg, qb, kb):
     e_dflt = oracle.rel_l2(oracle.attn_tiled(oracle.quant_qk(q, k), ref_v), exact)
     _log(f"  rel L2: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}  "
          f"default-oracle-vs-exact {e_dflt:.3e}")
-    assert e_or <= TOL_ORACLE
-    assert e_ex <= max(TOL_EXACT, e_dflt + TOL_ORACLE)
+    check_attention(got, tiled, ref_v["v_mean"], log=_log)
+    if cfg.name != "tiny":  # tiny: the method conflict recorded by test_tiny_exact_bar
+        assert e_ex <= TOL_EXACT
 
 
 @pytest.mark.parametrize("qb,kb", GRANS, ids=lambda g: str(g))
 def test_granularity_workload_sampled(sage, qb, kb):
     """FLUX joint shape at the finer granularities: quantised outputs bit-exact
-    in full, attention on every 16th query row."""
+    in full, attention on every 8th 32-query block plus the last."""
     cfg = synth.config(1)
     _log(f"[parity] q_block {qb} k_block {kb} workload {cfg.name} B{cfg.B} N{cfg.N} H{cfg.H} D{cfg.D}")
     q, k, v = synth.make_qkv(cfg)
@@ -332,13 +373,14 @@ def test_granularity_workload_sampled(sage, qb, kb):
     _check_quant_bits(qk, vq, ref_qk, ref_v, cfg.N)
     out = sage.attn_fwd(*qk[:4], *vq, N=cfg.N)
     torch.cuda.synchronize()
-    rows = synth.query_subset(cfg.N, every=16)
+    rows = synth.query_subset(cfg.N, every=8)
     got = _rows_gathered(out, rows)
     tiled = oracle.attn_tiled(ref_qk, ref_v, rows=rows)
     exact = oracle.attn_exact(q, k, v, rows=rows)
-    e_or, e_ex = oracle.rel_l2(got, tiled), oracle.rel_l2(got, exact)
-    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-oracle {e_or:.3e}  gpu-vs-exact {e_ex:.3e}")
-    assert e_or <= TOL_ORACLE and e_ex <= TOL_EXACT
+    e_ex = oracle.rel_l2(got, exact)
+    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-exact {e_ex:.3e}")
+    check_attention(got, tiled, ref_v["v_mean"], log=_log)
+    assert e_ex <= TOL_EXACT
 
 
 def test_plain_entry_points_equal_ex(sage):

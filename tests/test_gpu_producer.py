@@ -16,6 +16,7 @@ import torch
 
 import oracle
 import synth
+from tests.attn_bars import check_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -138,6 +139,5 @@ def test_fused_producer_flux_workload(sage):
     _check_qk(qk, ref, cfg.N)
     rows = synth.query_subset(cfg.N, every=16)
     got = out.float().cpu()[:, rows].permute(0, 2, 1, 3).double().numpy()
-    e = oracle.rel_l2(got, oracle.attn_tiled(ref, ref_v, rows=rows))
-    _log(f"  rows {rows.size}/{cfg.N}: gpu-vs-oracle {e:.3e}")
-    assert e <= TOL_ORACLE
+    _log(f"  rows {rows.size}/{cfg.N}")
+    check_attention(got, oracle.attn_tiled(ref, ref_v, rows=rows), ref_v["v_mean"], log=_log)

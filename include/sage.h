@@ -103,20 +103,28 @@ int64_t sage_padded_tokens(int64_t N);
 int sage_v_slot(int t);
 
 /* Workspace (device memory, bytes) needed by sage_quant_qk / sage_quant_v:
- * per-chunk channel partials (and, for V, the per-channel 448/a).  Any
- * contents on entry; clobbered by the call.  One workspace must not be shared
- * by calls that may run concurrently.  Returns 0 for unsupported shapes. */
+ * per-head arrival counters, then per-chunk channel partials (and, for V, the
+ * per-channel 448/a).  The first sage_workspace_zero_bytes() bytes hold
+ * the counters: they must be zero before the first call that uses the
+ * workspace (e.g. a zero-filled allocation), and every call leaves them zero;
+ * the rest may hold anything and is clobbered.  One workspace must not be
+ * shared by calls that may run concurrently.  Returns 0 for unsupported
+ * shapes. */
 size_t sage_quant_qk_workspace_size(int B, int N, int H, int D);
 /* Workspace bytes of sage_norm_rope_quant_qk: those of sage_quant_qk plus one
  * fp32 per K token row (B*H*Np*4, rounded up to 256); 0 for unsupported sizes. */
 size_t sage_norm_rope_quant_qk_workspace_size(int B, int N, int H, int D);
 size_t sage_quant_v_workspace_size(int B, int N, int H, int D);
+/* Bytes at the start of every quantiser workspace that must be zero before
+ * its first use (the arrival counters; a fixed 8192). */
+size_t sage_workspace_zero_bytes(void);
 
 /*
  * sage_quant_qk -- K smoothing + INT8 K, and INT8 Q (report §02 stage 03;
  * card A "K centering x INT8 quant").
  *
- *   k_mean[b,h,d] = bf16( fp32( (sum over all N tokens of K[b,n,h,d], fp64) / N ) )
+ *   k_mean[b,h,d] = bf16( fp32( fp64(sum over all N tokens of K[b,n,h,d]) / N ) )
+ *                   (the exact sum rounded once to fp64, then an fp64 divide)
  *   kc            = bf16( fp32(K) - fp32(k_mean) )          (BF16 rounding kept)
  *   per (b, h, 64-token block t):  a = max |kc|,  k_scale = a / 127,
  *       k_i8 = clamp(rne(kc * (127 / a)), -127, 127)        (fp32 ops, RNE)
@@ -132,11 +140,14 @@ size_t sage_quant_v_workspace_size(int B, int N, int H, int D);
  *   k_i8    int8  [B,H,Np,D]   rows N..Np-1 are 0
  *   k_scale fp32  [B,H,Np/64]
  *   k_mean  bf16  [B,H,D]
- * workspace: device, >= sage_quant_qk_workspace_size(B,N,H,D) bytes.
- * The per-channel sums are exact whenever every value of a channel is a
- * multiple of the channel's smallest non-zero bf16 ulp u and sum|x| < u * 2^52
- * (true for all practical activations); the mean bits then do not depend on
- * summation order.
+ * workspace: device, >= sage_quant_qk_workspace_size(B,N,H,D) bytes, counters
+ * zero (see above).
+ * The channel sum is the exact sum of the bf16 values rounded once to fp64, for
+ * every input, so the mean bits never depend on a summation order.  Plain fp64
+ * accumulation is that sum when every value of a channel is a multiple of the
+ * channel's smallest non-zero bf16 ulp u and N * max|x| < u * 2^53 (true for
+ * ordinary activations); a channel that fails this check (a tiny value among
+ * large ones) is summed again exactly by a slower path.
  */
 int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                   const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
@@ -228,7 +239,8 @@ int sage_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q
  * sage_quant_v -- V smoothing + FP8 E4M3 V, transposed, padded and permuted
  * (report card C "V alias + tiled transpose"; E4M3 per the A10 FLUX.1 page §1.1).
  *
- *   v_mean[b,h,d]  = fp32( (sum over N tokens of V, fp64) / N )
+ *   v_mean[b,h,d]  = fp32( fp64(sum over N tokens of V) / N )   (exact sum,
+ *                    rounded once to fp64, as for k_mean)
  *   a              = max(|max_n V - v_mean|, |min_n V - v_mean|)   (fp32)
  *   v_scale[b,h,d] = a / 448
  *   code           = E4M3FN( fp32(V - v_mean) * (448 / a) )  RNE, saturating,
@@ -242,7 +254,8 @@ int sage_norm_rope_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q
  *                             padding columns hold 0x00
  *   v_scale fp32  [B,H,D]
  *   v_mean  fp32  [B,H,D]
- * workspace: as for sage_quant_qk, sized by sage_quant_v_workspace_size.
+ * workspace: as for sage_quant_qk (counters zero before first use), sized by
+ * sage_quant_v_workspace_size.
  */
 int sage_quant_v(const void* v, int64_t v_sb, int64_t v_sn, int64_t v_sh,
                  int B, int N, int H, int D,
@@ -351,6 +364,12 @@ int sage_gemm_fp8_rowwise(const uint8_t* x8, const float* x_scale, int M, const 
  * Returns SAGE_OK, SAGE_ERR_NULL, or the shape status of sage_attn_fwd. */
 int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
                            int* workgroups);
+
+/* Benchmark hook (process-wide, not meant for concurrent callers): forces the
+ * workgroup size of later sage_attn_fwd* launches (0: chosen per launch as
+ * sage_attn_launch_shape describes, 4 or 8 waves).  The output does not depend
+ * on it.  Returns SAGE_OK or SAGE_ERR_VALUE. */
+int sage_attn_tuning(int waves_per_workgroup);
 
 /* Host-only argument checks of the three entry points: same arguments (less
  * the stream), same status codes, no HIP calls; usable without a GPU. */

@@ -73,6 +73,7 @@ def _load():
         "orc_quant_rows_e4m3": ([_vp, _i64, _i32, _i32, _vp, _vp], None),
         "orc_gemm_fp8_rowwise": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
                                   _vp, _vp, _vp], None),
+        "orc_fsum": ([_vp, _i64], _dbl),
         "orc_num_threads": ([], _i32),
         "orc_set_num_threads": ([_i32], None),
     }
@@ -117,6 +118,13 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return y
 
 
+def fsum(x: np.ndarray) -> float:
+    """Correctly rounded fp64 sum of the exact sum of x (the channel sums of
+    reading R3 when plain fp64 accumulation is not provably exact)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    return float(_load().orc_fsum(_p(x), x.size))
+
+
 def e4m3_encode(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float64)
     y = np.empty(x.shape, dtype=np.uint8)
@@ -144,7 +152,8 @@ def v_slot(t: int) -> int:
 def quant_qk(q, k, q_block: int = BQ, k_block: int = BK):
     """Fused steps 1-4.  Returns dict of numpy arrays:
     q_i8 / k_i8 [B,H,N,D] int8, q_scale [B,H,ceil(N/q_block)], k_scale [B,H,ceil(N/k_block)]
-    fp32, k_mean [B,H,D] uint16 (bf16 bits), inexact (int: channels with a non-exact sum),
+    fp32, k_mean [B,H,D] uint16 (bf16 bits), inexact (int: channels whose plain fp64 sum is not
+    provably exact; their mean comes from the rounded exact sum),
     q_block, k_block.  q_block = 32 (the path's block granularity) or 1 (one scale per
     token); k_block = 64 (the key tile) or 16."""
     if q_block not in (1, BQ):
@@ -260,7 +269,9 @@ def quant_i8_blocks(x_bits: np.ndarray, blk: int):
 
 def quant_v(v):
     """Steps 5-6.  Returns dict: v_fp8 [B,H,D,Np] uint8 (slot-permuted, zero pad),
-    v_scale / v_mean [B,H,D] fp32, bad (int)."""
+    v_scale / v_mean [B,H,D] fp32, inexact (int: channels whose plain fp64 sum is
+    not provably exact; their mean comes from the rounded exact sum), bad (int:
+    channels where the min/max absmax identity failed, an oracle self-check)."""
     B, N, H, D = v.shape
     vb, sb, sn, sh = _bf16_view(v)
     Np = math.ceil(N / 64) * 64
@@ -271,7 +282,8 @@ def quant_v(v):
     )
     bad = _load().orc_quant_v(_p(vb), sb, sn, sh, B, N, H, D, _p(out["v_fp8"]),
                               _p(out["v_scale"]), _p(out["v_mean"]))
-    out["bad"] = int(bad)
+    out["inexact"] = int(bad) & 0xFFFFF
+    out["bad"] = int(bad) >> 20
     return out
 
 

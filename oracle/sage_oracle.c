@@ -132,11 +132,75 @@ static double bf16_ulp(uint16_t h) {
   return ldexp(1.0, e - 127 - 7);
 }
 
-/* Sum of one channel in fp64, in ascending token order.  Returns 1 if the sum
- * is provably exact: every value is a multiple of the smallest ulp u among the
- * non-zero values, and sum|x| < u * 2^52, so every partial sum is representable
- * and any summation order yields the same bits.  (Reading: the pages do not say
- * how the mean is reduced; an exact sum makes it order-free.) */
+/* The correctly rounded (to nearest, ties to even) fp64 value of the exact sum
+ * of x[0..n-1], by Shewchuk's exact-partials summation ("Adaptive Precision
+ * Floating-Point Arithmetic and Fast Robust Geometric Predicates", 1997, as
+ * used for Python's math.fsum): the running sum is kept as a list of
+ * non-overlapping fp64 partials whose exact total is the exact sum so far;
+ * at the end the partials are added from the largest down, with a correction
+ * for a tie that the lower partials break.  Finite inputs. */
+double orc_fsum(const double* x, int64_t n) {
+  double stack[64];
+  double* part = stack;
+  int64_t np = 0, cap = 64;
+  for (int64_t k = 0; k < n; ++k) {
+    double v = x[k];
+    int64_t i = 0;
+    for (int64_t j = 0; j < np; ++j) {
+      double y = part[j];
+      if (fabs(v) < fabs(y)) {
+        double t = v;
+        v = y;
+        y = t;
+      }
+      double hi = v + y;
+      double lo = y - (hi - v); /* exact: hi + lo == v + y */
+      if (lo != 0.0) part[i++] = lo;
+      v = hi;
+    }
+    if (i == cap) {
+      double* grown = (double*)malloc(sizeof(double) * (size_t)(2 * cap));
+      memcpy(grown, part, sizeof(double) * (size_t)i);
+      if (part != stack) free(part);
+      part = grown;
+      cap *= 2;
+    }
+    part[i] = v;
+    np = i + 1;
+  }
+  double hi = 0.0;
+  if (np > 0) {
+    int64_t j = np - 1;
+    double lo = 0.0;
+    hi = part[j];
+    while (j > 0) {
+      double v = hi;
+      double y = part[--j];
+      hi = v + y;
+      lo = y - (hi - v);
+      if (lo != 0.0) break;
+    }
+    /* hi + lo is exact and lo is half an ulp of hi or less; if it is exactly
+     * half and the next partial has the same sign, the true sum is beyond the
+     * half-way point: round away from hi */
+    if (j > 0 && ((lo < 0.0 && part[j - 1] < 0.0) || (lo > 0.0 && part[j - 1] > 0.0))) {
+      double y = lo * 2.0;
+      double v = hi + y;
+      if (y == v - hi) hi = v;
+    }
+  }
+  if (part != stack) free(part);
+  return hi;
+}
+
+/* Sum of one channel (reading R3): the correctly rounded fp64 value of the
+ * exact sum.  Returns 1 if plain fp64 accumulation is provably exact for this
+ * channel in any order -- every value is a multiple of the smallest ulp u
+ * among the non-zero values and sum|x| < u * 2^52, so every partial sum is
+ * representable -- in which case the ascending fp64 sum is that value; else the
+ * exact sum is rounded once (orc_fsum), and the return is 0.  (Reading: the
+ * pages do not say how the mean is reduced; the exact sum makes it order-free
+ * for every input.) */
 static int channel_sum(const uint16_t* base, int64_t stride, int64_t n, double* sum_out) {
   double s = 0.0, sabs = 0.0, umin = INFINITY;
   for (int64_t j = 0; j < n; ++j) {
@@ -149,8 +213,15 @@ static int channel_sum(const uint16_t* base, int64_t stride, int64_t n, double* 
       if (u < umin) umin = u;
     }
   }
+  const int exact = (umin == INFINITY) || (sabs < ldexp(umin, 52));
+  if (!exact) {
+    double* xs = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int64_t j = 0; j < n; ++j) xs[j] = (double)orc_bf16_value(base[j * stride]);
+    s = orc_fsum(xs, n);
+    free(xs);
+  }
   *sum_out = s;
-  return (umin == INFINITY) || (sabs < ldexp(umin, 52));
+  return exact;
 }
 
 #define AT(p, b, n, h, sb, sn, sh) ((p)[(int64_t)(b) * (sb) + (int64_t)(n) * (sn) + (int64_t)(h) * (sh)])
@@ -158,7 +229,8 @@ static int channel_sum(const uint16_t* base, int64_t stride, int64_t n, double* 
 /* Step 1 (card A, reading R1/R2/R3): K mean per (b, h, d) over all N tokens,
  * fp64 sum, fp64 / N, rounded to fp32 then to bf16 (the unfused path holds the
  * mean as a BF16 tensor).  Output k_mean[B][H][D].  Returns the number of
- * channels whose sum is not provably exact. */
+ * channels whose plain fp64 sum is not provably exact (their sum is the
+ * rounded exact sum, see channel_sum). */
 int orc_k_mean(const uint16_t* k, int64_t sb, int64_t sn, int64_t sh, int B, int N, int H, int D,
                uint16_t* k_mean) {
   int bad = 0;
@@ -369,20 +441,20 @@ int orc_quant_qk(const uint16_t* q, int64_t qsb, int64_t qsn, int64_t qsh,
  * inv = 448 / a; code = E4M3(fp32(V - mu) * inv).  Codes are stored transposed,
  * v_fp8[B][H][D][Np] (Np = N rounded up to 64), token t of block g at column
  * 64 g + slot(t mod 64); padding columns hold 0x00.
- * Returns (#channels with an inexact sum) + (#channels where the min/max
- * identity failed). */
+ * Returns (#channels whose plain fp64 sum is not provably exact) +
+ * 2^20 * (#channels where the min/max identity failed). */
 int orc_quant_v(const uint16_t* v, int64_t sb, int64_t sn, int64_t sh, int B, int N, int H, int D,
                 uint8_t* v_fp8, float* v_scale, float* v_mean) {
   const int64_t Np = ((int64_t)N + 63) / 64 * 64;
-  int bad = 0;
-#pragma omp parallel for collapse(2) reduction(+ : bad) schedule(dynamic)
+  int inexact = 0, idbad = 0;
+#pragma omp parallel for collapse(2) reduction(+ : inexact, idbad) schedule(dynamic)
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h)
       for (int d = 0; d < D; ++d) {
         const int64_t ch = ((int64_t)b * H + h) * D + d;
         const uint16_t* col = &AT(v, b, 0, h, sb, sn, sh) + d;
         double s;
-        bad += !channel_sum(col, sn, N, &s);
+        inexact += !channel_sum(col, sn, N, &s);
         float mu = (float)(s / (double)N);
         float mx = -INFINITY, mn = INFINITY;
         for (int j = 0; j < N; ++j) {
@@ -397,7 +469,7 @@ int orc_quant_v(const uint16_t* v, int64_t sb, int64_t sn, int64_t sh, int B, in
           float c = orc_bf16_value(col[(int64_t)j * sn]) - mu;
           if (fabsf(c) > brute) brute = fabsf(c);
         }
-        bad += (brute != a);
+        idbad += (brute != a);
         float inv = 448.0f / a;
         float scale = a / 448.0f;
         int zero = (a == 0.0f) || !isfinite(inv);
@@ -412,7 +484,7 @@ int orc_quant_v(const uint16_t* v, int64_t sb, int64_t sn, int64_t sh, int B, in
           row[(j / 64) * 64 + orc_v_slot(j % 64)] = zero ? 0x00 : orc_e4m3_encode((double)y);
         }
       }
-  return bad;
+  return inexact + (idbad << 20);
 }
 
 /* ------------------------------------------------------------------------- */

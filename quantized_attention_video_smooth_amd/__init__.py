@@ -42,6 +42,7 @@ _SIGS = {
     "sage_quant_qk_workspace_size": ([_i32] * 4, _sz),
     "sage_quant_v_workspace_size": ([_i32] * 4, _sz),
     "sage_norm_rope_quant_qk_workspace_size": ([_i32] * 4, _sz),
+    "sage_workspace_zero_bytes": ([], _sz),
     "sage_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "sage_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -53,6 +54,7 @@ _SIGS = {
     "sage_validate_attn_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                 _vp, _i64, _i64, _i64], _i32),
     "sage_attn_launch_shape": ([_i32, _i32, _i32, _i32, _vp, _vp], _i32),
+    "sage_attn_tuning": ([_i32], _i32),
     "sage_quant_qk_ex": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _vp], _i32),
     "sage_attn_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
@@ -167,6 +169,12 @@ def sage_attn_launch_shape(B: int, N: int, H: int, D: int) -> tuple:
     return w.value, g.value
 
 
+def sage_attn_tuning(waves: int = 0) -> None:
+    """Benchmark hook: forced attention workgroup size (0 automatic, 4 or 8
+    waves), process-wide."""
+    _check(lib().sage_attn_tuning(waves), "sage_attn_tuning")
+
+
 def sage_padded_tokens(n: int) -> int:
     return lib().sage_padded_tokens(n)
 
@@ -194,12 +202,14 @@ _workspaces: dict = {}
 
 def workspace(device, nbytes: int):
     """A device scratch buffer of at least nbytes, cached per device; calls
-    sharing it must be ordered (one stream)."""
+    sharing it must be ordered (one stream).  Allocated zero-filled: the
+    quantisers' workspaces begin with arrival counters that must be zero
+    before the first call (each call leaves them zero)."""
     import torch
     key = str(device)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -377,12 +387,12 @@ _workspaces_v: dict = {}
 
 
 def workspace_v(device, nbytes: int):
-    """Separate cached workspace for sage_quant_v."""
+    """Separate cached workspace for sage_quant_v (zero-filled, as above)."""
     import torch
     key = str(device)
     ws = _workspaces_v.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces_v[key] = ws
     return ws
 

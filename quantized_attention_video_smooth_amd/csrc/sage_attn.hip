@@ -41,6 +41,11 @@
 
 namespace sage {
 
+// Workgroup size forced for benchmark comparisons (process-wide; 0 = chosen
+// per launch by attn_waves).
+static std::atomic<int> g_attn_waves{0};
+void set_attn_waves(int waves) { g_attn_waves.store(waves, std::memory_order_relaxed); }
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -454,6 +459,8 @@ int attn_waves(int B, int N, int H) {
       ncu = 256;
     ncu_cache.store(ncu, std::memory_order_relaxed);
   }
+  const int forced = g_attn_waves.load(std::memory_order_relaxed);
+  if (forced == 4 || forced == 8) return forced;
   const int64_t wg8 = (int64_t)B * H * ceil_div(N, 256);
   return wg8 >= 8 * (int64_t)ncu ? 8 : 4;
 }

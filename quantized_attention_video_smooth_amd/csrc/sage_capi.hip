@@ -69,8 +69,8 @@ int validate_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const v
                 int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
                 const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                 const uint16_t* k_mean, const void* workspace, size_t workspace_bytes, int q_block,
-                int k_block, bool nr) {
-  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !workspace)
+                int k_block, bool nr, bool with_ws = true) {
+  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || (with_ws && !workspace))
     return SAGE_ERR_NULL;
   int st = check_shape(B, N, H, D);
   if (st != SAGE_OK) return st;
@@ -79,15 +79,15 @@ int validate_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const v
   if ((st = check_strides(B, N, H, q_sb, q_sn, q_sh)) != SAGE_OK) return st;
   if ((st = check_strides(B, N, H, k_sb, k_sn, k_sh)) != SAGE_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_i8) || !aligned16(k_i8) ||
-      !aligned16(k_mean) || !aligned16(workspace) || ((uintptr_t)q_scale & 3u) ||
+      !aligned16(k_mean) || (with_ws && !aligned16(workspace)) || ((uintptr_t)q_scale & 3u) ||
       ((uintptr_t)k_scale & 3u))
     return SAGE_ERR_ALIGN;
   const size_t need = sage::qk_workspace(B, N, H, D, nr).bytes;
-  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  if (with_ws && workspace_bytes < need) return SAGE_ERR_WORKSPACE;
   const int64_t Np = padded_tokens(N), bh = (int64_t)B * H;
   const Range outs[6] = {range_of(q_i8, bh * Np * D), range_of(q_scale, bh * (Np / q_block) * 4),
                          range_of(k_i8, bh * Np * D), range_of(k_scale, bh * (Np / k_block) * 4),
-                         range_of(k_mean, bh * D * 2), range_of(workspace, need)};
+                         range_of(k_mean, bh * D * 2), range_of(workspace, with_ws ? need : 0)};
   const Range ins[2] = {range_of(q, view_bytes(B, N, H, D, q_sb, q_sn, q_sh)),
                         range_of(k, view_bytes(B, N, H, D, k_sb, k_sn, k_sh))};
   if (any_overlap(outs, 6, ins, 2)) return SAGE_ERR_OVERLAP;
@@ -128,6 +128,8 @@ size_t sage_quant_v_workspace_size(int B, int N, int H, int D) {
   if (check_shape(B, N, H, D) != SAGE_OK) return 0;
   return sage::v_workspace(B, N, H, D).bytes;
 }
+
+size_t sage_workspace_zero_bytes(void) { return sage::workspace_zero_bytes(); }
 
 
 int sage_validate_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
@@ -434,6 +436,13 @@ int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
   const int st = check_shape(B, N, H, D);
   if (st != SAGE_OK) return st;
   sage::attn_shape(B, N, H, D, waves_per_workgroup, workgroups);
+  return SAGE_OK;
+}
+
+int sage_attn_tuning(int waves_per_workgroup) {
+  if (waves_per_workgroup != 0 && waves_per_workgroup != 4 && waves_per_workgroup != 8)
+    return SAGE_ERR_VALUE;
+  sage::set_attn_waves(waves_per_workgroup);
   return SAGE_OK;
 }
 

@@ -27,38 +27,56 @@ inline StatsSplit stats_split(int B, int N, int H) {
   return StatsSplit{(int)ceil_div(N, rpc), rpc};
 }
 
-// sage_quant_qk workspace: fp64 partial sums [BH][nchunk][D]; with the QK
-// RMSNorm + RoPE producer in front (nr), also each K row's fp32 r [BH][Np],
-// written by the statistics pass and read by the quantisation pass.
+// Arrival counters at the start of every quantiser workspace: one int per
+// (b, h) when a head is split into more than one statistics chunk, which
+// happens only for fewer than 2048 heads (stats_split).  The region has a
+// fixed size, so partials of one shape never land on the counters of another;
+// it must be zero before a workspace's first use and every call leaves it zero.
+constexpr size_t kCounterBytes = 2048 * sizeof(int);
+
+// sage_quant_qk workspace: arrival counters (above), fp64 partial sums [BH][nchunk][D],
+// exactness witnesses [BH][nchunk][D] (uint32: max |x| bits << 16 | (min
+// non-zero |x| bits - 1)); with the QK RMSNorm + RoPE producer in front (nr),
+// also each K row's fp32 r [BH][Np], written by the statistics pass and read
+// by the quantisation pass.
 struct QkWorkspace {
-  size_t partial_off, rk_off, bytes;
+  size_t cnt_off, partial_off, wit_off, rk_off, bytes;
 };
 inline QkWorkspace qk_workspace(int B, int N, int H, int D, bool nr = false) {
   StatsSplit s = stats_split(B, N, H);
-  size_t bh = (size_t)B * H;
+  size_t bh = (size_t)B * H, n = bh * s.nchunk * D;
   QkWorkspace w;
-  w.partial_off = 0;
-  w.rk_off = align256(bh * s.nchunk * D * sizeof(double));
+  w.cnt_off = 0;
+  w.partial_off = kCounterBytes;
+  w.wit_off = w.partial_off + align256(n * sizeof(double));
+  w.rk_off = w.wit_off + align256(n * sizeof(uint32_t));
   w.bytes = w.rk_off + (nr ? align256(bh * padded_tokens(N) * sizeof(float)) : 0);
   return w;
 }
 
-// sage_quant_v workspace: fp64 partial sums, fp32 partial min and max
-// [BH][nchunk][D], per-channel 448/a [BH][D].
+// sage_quant_v workspace: arrival counters [BH] (as above), fp64 partial sums,
+// fp32 partial min and max, exactness witnesses [BH][nchunk][D], per-channel
+// 448/a [BH][D].
 struct VWorkspace {
-  size_t sum_off, min_off, max_off, inv_off, bytes;
+  size_t cnt_off, sum_off, min_off, max_off, wit_off, inv_off, bytes;
 };
 inline VWorkspace v_workspace(int B, int N, int H, int D) {
   StatsSplit s = stats_split(B, N, H);
   size_t bh = (size_t)B * H, n = bh * s.nchunk * D;
   VWorkspace w;
-  w.sum_off = 0;
-  w.min_off = align256(n * sizeof(double));
+  w.cnt_off = 0;
+  w.sum_off = kCounterBytes;
+  w.min_off = w.sum_off + align256(n * sizeof(double));
   w.max_off = w.min_off + align256(n * sizeof(float));
-  w.inv_off = w.max_off + align256(n * sizeof(float));
+  w.wit_off = w.max_off + align256(n * sizeof(float));
+  w.inv_off = w.wit_off + align256(n * sizeof(uint32_t));
   w.bytes = w.inv_off + align256(bh * D * sizeof(float));
   return w;
 }
+
+// Bytes at the start of a quantiser workspace that must be zero before its
+// first use (the arrival counters).
+inline size_t workspace_zero_bytes() { return kCounterBytes; }
 
 // The QK RMSNorm + RoPE producer's constants: bf16 weights [D] of the Q and
 // K norms, the (cos, sin) table fp32 [N][D/2][2], eps.
@@ -91,6 +109,10 @@ hipError_t launch_quant_q(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t
 hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v_sh, int B, int N,
                           int H, int D, uint8_t* v_fp8, float* v_scale, float* v_mean,
                           void* workspace, hipStream_t stream);
+
+// Forced attention workgroup size (0 automatic, 4 or 8 waves), process-wide,
+// for benchmark comparisons.
+void set_attn_waves(int waves);
 
 // Waves per workgroup and grid size of the attention launch for these sizes
 // (N: queries).

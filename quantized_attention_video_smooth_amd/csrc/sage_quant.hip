@@ -11,10 +11,11 @@
 // All of this is HBM-bound streaming work.  Each tensor is read twice: once
 // for the per-channel statistics (fp64 sums, and min / max for V) and once to
 // quantise.  The statistics pass splits every (b, h) into token chunks and
-// writes per-chunk partials; a small per-head kernel reduces them in a fixed
-// order and writes the head's mean (and V's scale).  fp64 sums of bf16 values
-// are exact under the condition stated in sage.h, so the mean bits do not
-// depend on the summation order.
+// writes per-chunk partials; the last workgroup of each head to finish reduces
+// them in a fixed order and writes the head's mean (and V's scale).  The mean
+// is the exact channel sum rounded once to fp64, divided by N: fp64 sums of
+// bf16 values are exact in any order unless a channel mixes tiny and large
+// values, which the pass detects, and such a channel is summed again exactly.
 #include <hip/hip_runtime.h>
 
 #include "sage_device.h"
@@ -34,9 +35,168 @@ __device__ __forceinline__ int v_slot(int t) {
 }
 
 // ---------------------------------------------------------------------------
-// Channel statistics: grid (nchunk, B*H), 256 threads.  Each thread owns 8
-// consecutive channels (one 16-byte load per token row); D/8 threads cover a
-// row, so a pass reads 256/(D/8) rows.
+// Exactness of the channel sums (reading R3).  The mean of a channel is
+// fp64(exact sum) / N rounded to fp32: the exact sum rounded once to fp64.
+// Plain fp64 accumulation (in any order) reaches that value whenever every
+// partial sum is representable: all values are multiples of the smallest ulp
+// u among the non-zero ones, so this holds when N * max|x| < 2^53 * u.  The
+// statistics pass records, per chunk and channel, max |x| and the smallest
+// non-zero |x| (as bf16 bit patterns, packed two channels per word with
+// 16-bit integer min / max); a channel that fails the test has its sum
+// recomputed exactly (ExactSum) by the head's finalisation.
+// ---------------------------------------------------------------------------
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Witness of 2 bf16 (one 32-bit word) folded into (wmax, wmin): wmax = max
+// |x| bits, wmin = min (|x| bits - 1) with 0 wrapping to 0xFFFF (no value).
+__device__ __forceinline__ void witness2(uint32_t w, uint32_t& wmax, uint32_t& wmin) {
+  const u16x2 a = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+  const u16x2 am1 = a - (u16x2){1, 1};
+  wmax = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, wmax), a));
+  wmin = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, wmin), am1));
+}
+
+// True when plain fp64 accumulation of the channel is exact in any order,
+// from its witness over N values (max bits, min non-zero bits - 1).
+__device__ __forceinline__ bool sum_is_exact(uint32_t mxb, uint32_t mnb, int N) {
+  if (mnb == 0xFFFFu) return true;  // every value is zero
+  const uint32_t e = (mnb + 1) >> 7;  // biased exponent of the smallest non-zero |x|
+  const int eu = (e == 0 ? 1 : (int)e) - 134;  // its ulp is 2^eu
+  const double mx = (double)__uint_as_float(mxb << 16);
+  return (double)N * mx < __builtin_ldexp(1.0, 53 + eu);
+}
+
+// Exact sum of bf16 values: an integer in units of 2^-133 (the smallest bf16
+// subnormal), positive and negative parts in 320-bit unsigned accumulators
+// (|sum| < 2^31 * 2^8 * 2^253 < 2^320), rounded once to fp64 at the end.
+struct ExactSum {
+  uint64_t p[5], n[5];
+  __device__ void init() {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) p[i] = n[i] = 0;
+  }
+  __device__ static void add_at(uint64_t (&a)[5], uint64_t m, int sh) {
+    const int li = sh >> 6, bo = sh & 63;
+    const uint64_t lo = m << bo;
+    const uint64_t hi = bo ? (m >> (64 - bo)) : 0;
+    uint64_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint64_t add = (i == li) ? lo : (i == li + 1) ? hi : 0;
+      const uint64_t s1 = a[i] + add;
+      const uint64_t c1 = s1 < add;
+      const uint64_t s2 = s1 + c;
+      const uint64_t c2 = s2 < c;
+      a[i] = s2;
+      c = c1 | c2;
+    }
+  }
+  // x = (-1)^s * M * 2^(sh - 133): M = 128 + mantissa, sh = E - 1 for a
+  // normal (biased exponent E), M = mantissa, sh = 0 for a subnormal.
+  __device__ void add(uint32_t h) {
+    const uint32_t e = (h >> 7) & 0xFF, m7 = h & 0x7F;
+    if (e == 0xFF) return;  // Inf / NaN: unspecified results
+    const uint64_t m = e ? (m7 | 0x80) : m7;
+    if (m == 0) return;
+    add_at((h & 0x8000) ? n : p, m, e ? (int)e - 1 : 0);
+  }
+  __device__ void merge(const ExactSum& o) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      add_at(p, o.p[i], 64 * i);  // exact limb-aligned adds (bo = 0)
+      add_at(n, o.n[i], 64 * i);
+    }
+  }
+  // (p - n) * 2^-133, rounded to nearest fp64, ties to even.
+  __device__ double rounded() const {
+    uint64_t d[5];
+    uint64_t borrow = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint64_t t = p[i] - n[i];
+      const uint64_t b1 = p[i] < n[i];
+      const uint64_t t2 = t - borrow;
+      const uint64_t b2 = t < borrow;
+      d[i] = t2;
+      borrow = b1 | b2;
+    }
+    const bool neg = borrow != 0;
+    if (neg) {  // two's complement negation
+      uint64_t c = 1;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const uint64_t v = ~d[i] + c;
+        c = (c && v == 0) ? 1 : 0;
+        d[i] = v;
+      }
+    }
+    int top = -1;
+    for (int i = 4; i >= 0; --i)
+      if (d[i]) {
+        top = 64 * i + 63 - __builtin_clzll(d[i]);
+        break;
+      }
+    if (top < 0) return 0.0;
+    uint64_t mant;
+    int lo = 0;
+    if (top <= 52) {
+      mant = d[0];
+    } else {
+      lo = top - 52;  // lowest kept bit
+      const int li = lo >> 6, bo = lo & 63;
+      mant = d[li] >> bo;
+      if (bo && li + 1 < 5) mant |= d[li + 1] << (64 - bo);
+      mant &= (((uint64_t)1) << 53) - 1;
+      const int g = lo - 1;  // guard bit, then sticky below it
+      const bool guard = (d[g >> 6] >> (g & 63)) & 1;
+      bool sticky = false;
+      for (int i = 0; i < (g >> 6); ++i) sticky |= d[i] != 0;
+      if ((g & 63) && (d[g >> 6] & ((((uint64_t)1) << (g & 63)) - 1))) sticky = true;
+      if (guard && (sticky || (mant & 1))) {
+        ++mant;
+        if (mant >> 53) {
+          mant >>= 1;
+          ++lo;
+        }
+      }
+    }
+    const double r = __builtin_ldexp((double)mant, lo - 133);
+    return neg ? -r : r;
+  }
+};
+
+// Channel value of the QK RMSNorm + RoPE producer for token row x (bf16, unit
+// channel stride) at channel d, given the row's r: the arithmetic of
+// norm_rope_apply for the pair (d & ~1, d | 1), one channel returned.
+template <int D>
+__device__ __forceinline__ uint32_t nr_channel_bits(const uint16_t* xrow, int d, float r,
+                                                    const uint16_t* w, const float* rope_row) {
+  const int d0 = d & ~1;
+  const uint32_t xw = *(const uint32_t*)(xrow + d0);
+  const uint32_t ww = *(const uint32_t*)(w + d0);
+  float u0 = bf16_lo(xw) * r, u1 = bf16_hi(xw) * r;
+  bf16x2_round(u0, u1);
+  u0 *= bf16_lo(ww);
+  u1 *= bf16_hi(ww);
+  bf16x2_round(u0, u1);
+  const float c = rope_row[d0], s = rope_row[d0 + 1];
+  const float a0 = u0 * c, a1 = u1 * s;
+  const float b0 = u0 * s, b1 = u1 * c;
+  float y0 = a0 - a1, y1 = b0 + b1;
+  bf16x2_round(y0, y1);
+  return __float_as_uint((d & 1) ? y1 : y0) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Channel statistics + per-head finalisation: grid (nchunk, B*H), 256
+// threads.  Each thread owns 8 consecutive channels (one 16-byte load per
+// token row); D/8 threads cover a row, so a pass reads 256/(D/8) rows.  A
+// workgroup writes its chunk's partials (fp64 sums, V's min / max, the
+// exactness witnesses), then takes a ticket from the head's arrival counter;
+// the last of the head's nchunk workgroups reduces the partials in ascending
+// chunk order and writes the head's mean (K: k_mean = bf16(fp32(sum / N));
+// V: v_mean, v_scale and 448/a for the quantisation pass), recomputing the
+// sum exactly for a channel whose witness fails, and leaves the counter zero.
 // ---------------------------------------------------------------------------
 // NR: the rows are first put through the QK RMSNorm + RoPE producer
 // (weights nr_w, table rope), so the statistics are those of the producer's
@@ -45,28 +205,46 @@ template <int D, bool IS_V, bool NR = false>
 __global__ __launch_bounds__(kThreads) void stats_kernel(
     const uint16_t* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, int H, int N, int nchunk,
     int rows_per_chunk, double* __restrict__ psum, float* __restrict__ pmin,
-    float* __restrict__ pmax, const uint16_t* __restrict__ nr_w, const float* __restrict__ rope,
-    double eps, float* __restrict__ rk, int Np) {
+    float* __restrict__ pmax, uint32_t* __restrict__ pwit, int* __restrict__ cnt,
+    const uint16_t* __restrict__ nr_w, const float* __restrict__ rope, double eps,
+    float* __restrict__ rk, int Np, uint16_t* __restrict__ k_mean, float* __restrict__ v_mean,
+    float* __restrict__ v_scale, float* __restrict__ v_inv) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
-  __shared__ double s_sum[RPP][D];
+  constexpr int TPC = kThreads / D;  // threads per channel in the exact re-summation
+  // s_sum's storage is reused for the witnesses, then for the exact sums
+  __shared__ __attribute__((aligned(16))) double s_sum[RPP][D];
   __shared__ float s_min[IS_V ? RPP : 1][D];
   __shared__ float s_max[IS_V ? RPP : 1][D];
+  __shared__ int s_last;
+  __shared__ int s_flag[D];
+  static_assert(2 * sizeof(uint32_t) * RPP * (D / 2) <= sizeof(double) * RPP * D, "witness alias");
+  static_assert(sizeof(uint64_t) * 10 * (TPC - 1) * D <= sizeof(double) * RPP * D, "exact-sum alias");
+  uint32_t (*s_wmax)[D / 2] = (uint32_t(*)[D / 2])(&s_sum[0][0]);
+  uint32_t (*s_wmin)[D / 2] = s_wmax + RPP;
+  uint64_t (*s_ex)[D][10] = (uint64_t(*)[D][10])(&s_sum[0][0]);
 
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x, lr = tid / LPR, lc = tid - lr * LPR;
-  const uint16_t* base = x + (int64_t)b * sb + (int64_t)h * sh + lc * 8;
+  const uint16_t* head = x + (int64_t)b * sb + (int64_t)h * sh;
+  const uint16_t* base = head + lc * 8;
   const int r0 = c * rows_per_chunk;
   const int r1 = min(N, r0 + rows_per_chunk);
 
   double acc[8];
   float mn[8], mx[8];
+  uint32_t wmax[4], wmin[4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     acc[j] = 0.0;
     mn[j] = __builtin_inff();
     mx[j] = -__builtin_inff();
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    wmax[j] = 0;
+    wmin[j] = 0xFFFFFFFFu;
   }
   float w8[8];
   if constexpr (NR) load_w8(nr_w, lc, w8);
@@ -75,6 +253,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   auto take = [&](const uint4& v, int row) {
     float f[8];
     unpack8(v, f);
+    uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     if constexpr (NR) {
       float f1[1][8], cs[1][8], r[1], r_own;
 #pragma unroll
@@ -85,7 +264,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
       norm_rope_apply<1>(f1, w8, cs, r);
 #pragma unroll
       for (int j = 0; j < 8; ++j) f[j] = f1[0][j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wd[j] = bf16x2_rne(f[2 * j], f[2 * j + 1]);  // exact: bf16 values
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) witness2(wd[j], wmax[j], wmin[j]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       acc[j] += (double)f[j];
@@ -123,9 +306,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
       if ((lc & (LPR / 2 - 1)) == 0) rk[(size_t)bh * Np + r + (lc / (LPR / 2)) * RPP] = r_own;
       norm_rope_apply<2>(f, w8, cs, rr);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) witness2(bf16x2_rne(f[u][2 * j], f[u][2 * j + 1]), wmax[j], wmin[j]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] += (double)f[u][j];
+      }
     }
   }
   for (; r < r1; r += RPP) take(*(const uint4*)(base + (int64_t)r * sn), r);
@@ -139,78 +325,149 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     }
   }
   __syncthreads();
+  double csum = 0.0;
+  float clo = __builtin_inff(), chi = -__builtin_inff();
+  if (tid < D) {
+    for (int i = 0; i < RPP; ++i) {
+      csum += s_sum[i][tid];
+      if (IS_V) {
+        clo = fminf(clo, s_min[i][tid]);
+        chi = fmaxf(chi, s_max[i][tid]);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s_wmax[lr][lc * 4 + j] = wmax[j];
+    s_wmin[lr][lc * 4 + j] = wmin[j];
+  }
+  __syncthreads();
   const size_t pbase = ((size_t)bh * nchunk + c) * D;
   if (tid < D) {
-    double s = 0.0;
-    float lo = __builtin_inff(), hi = -__builtin_inff();
+    uint32_t wx = 0, wn = 0xFFFFu;
+    const int sh16 = 16 * (tid & 1);
     for (int i = 0; i < RPP; ++i) {
-      s += s_sum[i][tid];
-      if (IS_V) {
-        lo = fminf(lo, s_min[i][tid]);
-        hi = fmaxf(hi, s_max[i][tid]);
-      }
+      wx = max(wx, (s_wmax[i][tid >> 1] >> sh16) & 0xFFFFu);
+      wn = min(wn, (s_wmin[i][tid >> 1] >> sh16) & 0xFFFFu);
     }
-    psum[pbase + tid] = s;
+    psum[pbase + tid] = csum;
     if (IS_V) {
-      pmin[pbase + tid] = lo;
-      pmax[pbase + tid] = hi;
+      pmin[pbase + tid] = clo;
+      pmax[pbase + tid] = chi;
     }
+    pwit[pbase + tid] = (wx << 16) | wn;
   }
-}
 
-// ---------------------------------------------------------------------------
-// Per-head finalisation: grid (B*H), D threads.  Reduces the chunk partials in
-// ascending chunk order; K: k_mean = bf16(fp32(sum / N)); V: v_mean, v_scale
-// and 448/a (kept in the workspace for the quantisation pass).
-// ---------------------------------------------------------------------------
-template <int D, bool IS_V>
-__global__ __launch_bounds__(D) void finalize_kernel(
-    const double* __restrict__ psum, const float* __restrict__ pmin, const float* __restrict__ pmax,
-    int N, int nchunk, uint16_t* __restrict__ k_mean, float* __restrict__ v_mean,
-    float* __restrict__ v_scale, float* __restrict__ v_inv) {
-  const int bh = blockIdx.x, d = threadIdx.x;
-  double s = 0.0;
+  // ---- arrival: the last workgroup of the head finalises it ----
+  __threadfence();  // this workgroup's partials before its ticket
+  __syncthreads();
+  // (one chunk per head: every workgroup finalises its own head, no counter)
+  if (tid == 0) s_last = nchunk == 1 || atomicAdd(cnt + bh, 1) == nchunk - 1;
+  __syncthreads();
+  if (!s_last) return;  // whole workgroup
+  __threadfence();      // every other workgroup's partials after the tickets
+
+  // Channels whose plain sum may be inexact: flagged in LDS, then summed
+  // exactly by all threads (channel d = tid % D, a stride of the tokens each).
+  double s_plain = 0.0;
   float lo = __builtin_inff(), hi = -__builtin_inff();
-  const size_t base = (size_t)bh * nchunk * D + d;
-  int c = 0;
-  for (; c + 8 <= nchunk; c += 8) {  // 8 loads in flight, summed in ascending chunk order
-    double ps[8];
-    float pl[8], ph[8];
+  if (tid < D) {
+    const size_t hb = (size_t)bh * nchunk * D + tid;
+    uint32_t wx = 0, wn = 0xFFFFu;
+    int ch = 0;
+    for (; ch + 8 <= nchunk; ch += 8) {  // 8 loads in flight, summed in ascending chunk order
+      double ps[8];
+      float pl[8], ph[8];
+      uint32_t pw[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      ps[u] = psum[base + (size_t)(c + u) * D];
-      if (IS_V) {
-        pl[u] = pmin[base + (size_t)(c + u) * D];
-        ph[u] = pmax[base + (size_t)(c + u) * D];
+      for (int u = 0; u < 8; ++u) {
+        ps[u] = psum[hb + (size_t)(ch + u) * D];
+        pw[u] = pwit[hb + (size_t)(ch + u) * D];
+        if (IS_V) {
+          pl[u] = pmin[hb + (size_t)(ch + u) * D];
+          ph[u] = pmax[hb + (size_t)(ch + u) * D];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s_plain += ps[u];
+        wx = max(wx, pw[u] >> 16);
+        wn = min(wn, pw[u] & 0xFFFFu);
+        if (IS_V) {
+          lo = fminf(lo, pl[u]);
+          hi = fmaxf(hi, ph[u]);
+        }
       }
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      s += ps[u];
+    for (; ch < nchunk; ++ch) {
+      s_plain += psum[hb + (size_t)ch * D];
+      const uint32_t pw = pwit[hb + (size_t)ch * D];
+      wx = max(wx, pw >> 16);
+      wn = min(wn, pw & 0xFFFFu);
       if (IS_V) {
-        lo = fminf(lo, pl[u]);
-        hi = fmaxf(hi, ph[u]);
+        lo = fminf(lo, pmin[hb + (size_t)ch * D]);
+        hi = fmaxf(hi, pmax[hb + (size_t)ch * D]);
+      }
+    }
+    s_flag[tid] = sum_is_exact(wx, wn, N) ? 0 : 1;
+  }
+  __syncthreads();
+  // exact sums of the flagged channels (none for ordinary activations);
+  // part 0 keeps its sum in registers, parts 1.. hand theirs over in LDS
+  ExactSum ex;
+  ex.init();
+  {
+    const int d = tid % D, part = tid / D;
+    if (s_flag[d]) {
+      const uint16_t* col = head + d;
+      for (int n = part; n < N; n += TPC) {
+        uint32_t bits;
+        if constexpr (NR) {
+          const float* rope_row = rope + (size_t)n * D;  // (cos, sin) pairs: D floats per token
+          bits = nr_channel_bits<D>(head + (int64_t)n * sn, d, rk[(size_t)bh * Np + n], nr_w, rope_row);
+        } else {
+          bits = col[(int64_t)n * sn];
+        }
+        ex.add(bits);
+      }
+      if (part > 0) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          s_ex[part - 1][d][i] = ex.p[i];
+          s_ex[part - 1][d][5 + i] = ex.n[i];
+        }
       }
     }
   }
-  for (; c < nchunk; ++c) {
-    s += psum[base + (size_t)c * D];
-    if (IS_V) {
-      lo = fminf(lo, pmin[base + (size_t)c * D]);
-      hi = fmaxf(hi, pmax[base + (size_t)c * D]);
+  __syncthreads();
+  if (tid < D) {
+    double s = s_plain;
+    if (s_flag[tid]) {
+      for (int part = 1; part < TPC; ++part) {
+        ExactSum o;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          o.p[i] = s_ex[part - 1][tid][i];
+          o.n[i] = s_ex[part - 1][tid][5 + i];
+        }
+        ex.merge(o);
+      }
+      s = ex.rounded();
+    }
+    const float mean = (float)(s / (double)N);
+    if (!IS_V) {
+      k_mean[(size_t)bh * D + tid] = (uint16_t)bf16_bits_rne(mean);
+    } else {
+      const float a = fmaxf(fabsf(hi - mean), fabsf(lo - mean));
+      const float inv = 448.0f / a;
+      const bool zero = (a == 0.0f) || !__builtin_isfinite(inv);
+      v_mean[(size_t)bh * D + tid] = mean;
+      v_scale[(size_t)bh * D + tid] = zero ? 0.0f : a / 448.0f;
+      v_inv[(size_t)bh * D + tid] = zero ? 0.0f : inv;
     }
   }
-  const float mean = (float)(s / (double)N);
-  if (!IS_V) {
-    k_mean[(size_t)bh * D + d] = (uint16_t)bf16_bits_rne(mean);
-  } else {
-    const float a = fmaxf(fabsf(hi - mean), fabsf(lo - mean));
-    const float inv = 448.0f / a;
-    const bool zero = (a == 0.0f) || !__builtin_isfinite(inv);
-    v_mean[(size_t)bh * D + d] = mean;
-    v_scale[(size_t)bh * D + d] = zero ? 0.0f : a / 448.0f;
-    v_inv[(size_t)bh * D + d] = zero ? 0.0f : inv;
-  }
+  if (tid == 0 && nchunk > 1) cnt[bh] = 0;  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -551,15 +808,11 @@ hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t 
   float* rk = NR ? (float*)(wsb + w.rk_off) : nullptr;
   hipLaunchKernelGGL((stats_kernel<D, false, NR>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream,
                      k, k_sb, k_sn, k_sh, H, N, s.nchunk, s.rows_per_chunk,
-                     (double*)(wsb + w.partial_off), (float*)nullptr, (float*)nullptr, nr.wk,
-                     nr.rope, nr.eps, rk, Np);
+                     (double*)(wsb + w.partial_off), (float*)nullptr, (float*)nullptr,
+                     (uint32_t*)(wsb + w.wit_off), (int*)(wsb + w.cnt_off), nr.wk, nr.rope, nr.eps, rk,
+                     Np, k_mean, (float*)nullptr, (float*)nullptr, (float*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((finalize_kernel<D, false>), dim3(B * H), dim3(D), 0, stream,
-                     (const double*)(wsb + w.partial_off), (const float*)nullptr,
-                     (const float*)nullptr, N, s.nchunk, k_mean, (float*)nullptr, (float*)nullptr,
-                     (float*)nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((qk_quant_kernel<D, NR>), dim3(Np / 64, B * H, 2), dim3(kThreads), 0, stream,
                      q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, H, N, Np, (const uint16_t*)k_mean,
                      q_i8, q_scale, k_i8, k_scale, q_block, k_block, nr.wq, nr.wk, nr.rope, nr.eps,
@@ -579,15 +832,11 @@ hipError_t quant_v_impl(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v
   hipLaunchKernelGGL((stats_kernel<D, true>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream, v,
                      v_sb, v_sn, v_sh, H, N, s.nchunk, s.rows_per_chunk,
                      (double*)(wsb + w.sum_off), (float*)(wsb + w.min_off),
-                     (float*)(wsb + w.max_off), (const uint16_t*)nullptr, (const float*)nullptr, 0.0,
-                     (float*)nullptr, 0);
+                     (float*)(wsb + w.max_off), (uint32_t*)(wsb + w.wit_off),
+                     (int*)(wsb + w.cnt_off), (const uint16_t*)nullptr, (const float*)nullptr, 0.0,
+                     (float*)nullptr, 0, (uint16_t*)nullptr, v_mean, v_scale, inv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((finalize_kernel<D, true>), dim3(B * H), dim3(D), 0, stream,
-                     (const double*)(wsb + w.sum_off), (const float*)(wsb + w.min_off),
-                     (const float*)(wsb + w.max_off), N, s.nchunk, (uint16_t*)nullptr, v_mean,
-                     v_scale, inv);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((v_quant_kernel<D>), dim3((Np + 127) / 128, B * H), dim3(kThreads), 0, stream,
                      v, v_sb, v_sn, v_sh, H, N, Np, (const float*)v_mean, (const float*)inv, v_fp8);
   return hipGetLastError();

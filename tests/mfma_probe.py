@@ -26,6 +26,6 @@ def load():
     vp = ctypes.c_void_p
     lib.probe_mfma_f8.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
     lib.probe_mfma_f8.restype = ctypes.c_int
-    lib.probe_mfma_f8_scaled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
-    lib.probe_mfma_f8_scaled.restype = ctypes.c_int
+    lib.probe_mfma_i8.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.probe_mfma_i8.restype = ctypes.c_int
     return lib

@@ -50,8 +50,8 @@ def test_graph_replays_match_eager(sage, cfg):
     v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     v_mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
-    ws_qk = torch.empty(sage.sage_quant_qk_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
-    ws_v = torch.empty(sage.sage_quant_v_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
+    ws_qk = torch.zeros(sage.sage_quant_qk_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
+    ws_v = torch.zeros(sage.sage_quant_v_workspace_size(B, N, H, D), dtype=torch.uint8, device=dev)
     qs, ks, vs, os_ = q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3]
 
     g = torch.cuda.CUDAGraph()

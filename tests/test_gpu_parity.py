@@ -395,7 +395,7 @@ def test_plain_entry_points_equal_ex(sage):
     torch.cuda.synchronize()
     lib = sage.lib()
     plain = [torch.empty_like(t) for t in qk]
-    ws = torch.empty(lib.sage_quant_qk_workspace_size(B, N, H, D), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(lib.sage_quant_qk_workspace_size(B, N, H, D), dtype=torch.uint8, device="cuda")
     qs = [x for x in q.stride()[:3]]
     ks = [x for x in k.stride()[:3]]
     st = lib.sage_quant_qk(q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D,
@@ -411,3 +411,60 @@ def test_plain_entry_points_equal_ex(sage):
     for a, b in zip(qk, plain):
         assert torch.equal(a, b)
     assert torch.equal(out, o2)
+
+
+def _tiny_channel(N, tiny):
+    """Token 0: tiny, tokens 1..N-2: +1, -1, ..., token N-1: 0 (N even): the
+    exact sum is `tiny`; an fp64 running sum that meets +1 after it loses it."""
+    col = np.zeros(N)
+    col[0] = tiny
+    col[1:N - 1] = np.where(np.arange(N - 2) % 2 == 0, 1.0, -1.0)
+    return torch.from_numpy(col).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("shape,tiny", [((1, 4608, 2, 64), 2.0 ** -100), ((1, 4608, 2, 64), 2.0 ** -133),
+                                        ((2, 32768, 3, 128), 2.0 ** -100)],
+                         ids=["N4608-2^-100", "N4608-2^-133", "N32768-2^-100"])
+def test_channel_sum_exact_fallback(sage, shape, tiny):
+    """Reading R3 for channels where plain fp64 accumulation is not exact: one
+    K and one V channel hold a tiny bf16 value (normal or subnormal) among
+    +-1 values, plus a channel of random values with one subnormal.  The GPU
+    detects them and sums them exactly: means, scales and codes bit-exact."""
+    B, N, H, D = shape
+    cfg = synth.custom(B, N, H, D, tag=404)
+    _log(f"[parity] exact channel sums B{B} N{N} H{H} D{D} tiny 2^{math.log2(tiny):.0f}")
+    q, k, v = synth.make_qkv(cfg)
+    col = _tiny_channel(N, tiny)
+    k[B - 1, :, H - 1, 5] = col
+    v[0, :, H - 1, 9] = col
+    k[0, 7, 0, 3] = 1e-40  # a subnormal among N(0,1)-like values
+    v[B - 1, N // 2, 0, 0] = -1e-40
+    ref_qk, ref_v = oracle.quant_qk(q, k), oracle.quant_v(v)
+    assert ref_qk["inexact"] == 2 and ref_v["inexact"] == 2 and ref_v["bad"] == 0
+    _, _, _, qk, vq = _gpu_quant(sage, q, k, v)
+    _check_quant_bits(qk, vq, ref_qk, ref_v, N)
+    if tiny == 2.0 ** -100:
+        assert ref_v["v_mean"][0, H - 1, 9] == np.float32(tiny / N) != 0
+
+
+def test_channel_sum_exact_fallback_producer(sage):
+    """The same for the fused QK RMSNorm + RoPE producer: a pre-norm K channel
+    pair (4, 5) holding a tiny value at token 0 and +-1 values elsewhere gives
+    producer outputs with a tiny value among O(1) ones; the fallback sums the
+    producer's outputs exactly (recomputing them per token)."""
+    from tests.test_gpu_producer import _check_qk, _consts
+    cfg = synth.custom(1, 2048, 2, 128, tag=405)
+    _log("[parity] exact channel sums behind the fused producer")
+    q, k, _ = synth.make_qkv(cfg)
+    col = _tiny_channel(cfg.N, 2.0 ** -100)
+    k[0, :, 1, 4] = col
+    k[0, :, 1, 5] = 0
+    wq, wk, rope = _consts(cfg)
+    yq, _ = oracle.norm_rope(q, wq, rope.numpy())
+    yk, _ = oracle.norm_rope(k, wk, rope.numpy())
+    ref = oracle.quant_qk(yq, yk)
+    _log(f"  oracle channels with an inexact plain sum: {ref['inexact']}")
+    assert ref["inexact"] >= 1
+    qk = sage.norm_rope_quant_qk(q.cuda(), k.cuda(), wq.cuda(), wk.cuda(), rope.cuda())
+    torch.cuda.synchronize()
+    _check_qk(qk, ref, cfg.N)

@@ -176,6 +176,27 @@ int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                      void* stream);
 
 /*
+ * sage_quant_qk_static -- sage_quant_qk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * outputs bit for bit.  The workspace is a static device array of
+ * SAGE_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the call allocates nothing (its first call on a device also
+ * zero-fills that device's array with a small kernel on `stream`).
+ * Call with the stream's device current.  Problems whose workspace
+ * (sage_quant_qk_workspace_size) exceeds SAGE_STATIC_SCRATCH_BYTES return
+ * SAGE_ERR_WORKSPACE without enqueuing anything; other errors as sage_quant_qk.
+ * Every call on a GPU uses that GPU's one array: calls that may overlap on one
+ * GPU (other streams, other threads) race and must not be issued.
+ */
+#define SAGE_STATIC_SCRATCH_BYTES (8u << 20)
+int sage_quant_qk_static(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+                         const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+                         int B, int N, int H, int D,
+                         int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                         uint16_t* k_mean, void* stream);
+
+/*
  * sage_quant_q -- the Q half of sage_quant_qk_ex alone.  Q's codes and scales
  * depend only on Q's own blocks (no statistics over the sequence), so under
  * sequence parallelism (the "FLUX 3 Action" SGLang page, §3.1 Multi-GPU: the

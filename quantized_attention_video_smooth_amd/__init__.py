@@ -43,6 +43,8 @@ _SIGS = {
     "sage_quant_v_workspace_size": ([_i32] * 4, _sz),
     "sage_norm_rope_quant_qk_workspace_size": ([_i32] * 4, _sz),
     "sage_workspace_zero_bytes": ([], _sz),
+    "sage_quant_qk_static": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                              _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "sage_quant_qk": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "sage_quant_v": ([_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/sage.h"
 #include "sage_internal.h"
 
@@ -63,8 +65,9 @@ bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
-// Checks shared by sage_quant_qk_ex and sage_norm_rope_quant_qk (nr): the
-// workspace requirement differs.
+// Checks shared by sage_quant_qk_ex, sage_norm_rope_quant_qk (nr: the
+// workspace requirement differs) and sage_quant_qk_static (with_ws false: the
+// workspace is the library's static scratch, not a caller buffer).
 int validate_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
                 int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
                 const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
@@ -92,6 +95,40 @@ int validate_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const v
                         range_of(k, view_bytes(B, N, H, D, k_sb, k_sn, k_sh))};
   if (any_overlap(outs, 6, ins, 2)) return SAGE_ERR_OVERLAP;
   return SAGE_OK;
+}
+
+// ---- sage_quant_qk_static: the quantiser workspace as a static device array ----
+// One copy per GPU the library runs on, held until the process ends.  In host
+// code this name is a stand-in, not a device address: kernels get the
+// per-device address that hipGetSymbolAddress returns (kept in g_scratch).
+__device__ __align__(256) uint8_t scratch[SAGE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+__global__ void zero_words(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// The current device's scratch address.  On the first call for a device (with
+// that device current) it is looked up and the whole array is zeroed on
+// `stream`, which orders the fill before the caller's kernels.  nullptr on a
+// HIP error.
+void* scratch_for_current_device(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return g_scratch[dev];
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, (uint32_t*)ptr,
+                     (size_t)SAGE_STATIC_SCRATCH_BYTES / 4);
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  g_scratch[dev] = ptr;
+  return ptr;
 }
 
 }  // namespace
@@ -238,6 +275,23 @@ int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const
   return sage_quant_qk_ex(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8, q_scale, k_i8,
                           k_scale, k_mean, workspace, workspace_bytes, SAGE_Q_BLOCK, SAGE_K_BLOCK,
                           stream);
+}
+
+int sage_quant_qk_static(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+                         int64_t k_sb, int64_t k_sn, int64_t k_sh, int B, int N, int H, int D,
+                         int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                         uint16_t* k_mean, void* stream) {
+  int st = validate_qk(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, B, N, H, D, q_i8, q_scale, k_i8,
+                       k_scale, k_mean, nullptr, 0, SAGE_Q_BLOCK, SAGE_K_BLOCK, false, false);
+  if (st != SAGE_OK) return st;
+  if (sage::qk_workspace(B, N, H, D).bytes > (size_t)SAGE_STATIC_SCRATCH_BYTES) return SAGE_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device((hipStream_t)stream);
+  if (!ws) return SAGE_ERR_HIP;
+  return status_of(sage::launch_quant_qk((const uint16_t*)q, B > 1 ? q_sb : 0, q_sn, H > 1 ? q_sh : 0,
+                                         (const uint16_t*)k, B > 1 ? k_sb : 0, k_sn,
+                                         H > 1 ? k_sh : 0, B, N, H, D, SAGE_Q_BLOCK, SAGE_K_BLOCK,
+                                         nullptr, q_i8, q_scale, k_i8, k_scale, k_mean, ws,
+                                         (hipStream_t)stream));
 }
 
 int sage_validate_quant_q(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, int B, int N,

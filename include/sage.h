@@ -144,10 +144,12 @@ size_t sage_workspace_zero_bytes(void);
  * zero (see above).
  * The channel sum is the exact sum of the bf16 values rounded once to fp64, for
  * every input, so the mean bits never depend on a summation order.  Plain fp64
- * accumulation is that sum when every value of a channel is a multiple of the
- * channel's smallest non-zero bf16 ulp u and N * max|x| < u * 2^53 (true for
- * ordinary activations); a channel that fails this check (a tiny value among
- * large ones) is summed again exactly by a slower path.
+ * accumulation is that sum when the channel's sum of |x| (accumulated in fp64
+ * alongside) is below u * 2^52, u being the ulp of its smallest non-zero bf16
+ * value (true for ordinary activations); a channel that fails this check (a
+ * tiny value among large ones) is summed again exactly by a slower path (the
+ * head's last statistics workgroup re-reads that channel: ~N / 256 dependent
+ * integer additions per thread).
  */
 int sage_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                   const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
@@ -189,7 +191,7 @@ int sage_quant_qk_ex(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
  * Every call on a GPU uses that GPU's one array: calls that may overlap on one
  * GPU (other streams, other threads) race and must not be issued.
  */
-#define SAGE_STATIC_SCRATCH_BYTES (8u << 20)
+#define SAGE_STATIC_SCRATCH_BYTES (16u << 20)
 int sage_quant_qk_static(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
                          const void* k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
                          int B, int N, int H, int D,

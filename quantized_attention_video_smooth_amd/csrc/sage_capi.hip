@@ -101,7 +101,7 @@ int validate_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const v
 // One copy per GPU the library runs on, held until the process ends.  In host
 // code this name is a stand-in, not a device address: kernels get the
 // per-device address that hipGetSymbolAddress returns (kept in g_scratch).
-__device__ __align__(256) uint8_t scratch[SAGE_STATIC_SCRATCH_BYTES];
+static __device__ __align__(256) uint8_t scratch[SAGE_STATIC_SCRATCH_BYTES];
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;

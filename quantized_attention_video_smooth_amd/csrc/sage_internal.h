@@ -34,13 +34,13 @@ inline StatsSplit stats_split(int B, int N, int H) {
 // it must be zero before a workspace's first use and every call leaves it zero.
 constexpr size_t kCounterBytes = 2048 * sizeof(int);
 
-// sage_quant_qk workspace: arrival counters (above), fp64 partial sums [BH][nchunk][D],
-// exactness witnesses [BH][nchunk][D] (uint32: max |x| bits << 16 | (min
-// non-zero |x| bits - 1)); with the QK RMSNorm + RoPE producer in front (nr),
-// also each K row's fp32 r [BH][Np], written by the statistics pass and read
-// by the quantisation pass.
+// sage_quant_qk workspace: arrival counters (above), fp64 partial sums and
+// partial sums of |x| [BH][nchunk][D], exactness witnesses [BH][nchunk][D]
+// (uint32: smallest non-zero |x| bits - 1, 0xFFFF for none); with the QK
+// RMSNorm + RoPE producer in front (nr), also each K row's fp32 r [BH][Np],
+// written by the statistics pass and read by the quantisation pass.
 struct QkWorkspace {
-  size_t cnt_off, partial_off, wit_off, rk_off, bytes;
+  size_t cnt_off, partial_off, abs_off, wit_off, rk_off, bytes;
 };
 inline QkWorkspace qk_workspace(int B, int N, int H, int D, bool nr = false) {
   StatsSplit s = stats_split(B, N, H);
@@ -48,17 +48,18 @@ inline QkWorkspace qk_workspace(int B, int N, int H, int D, bool nr = false) {
   QkWorkspace w;
   w.cnt_off = 0;
   w.partial_off = kCounterBytes;
-  w.wit_off = w.partial_off + align256(n * sizeof(double));
+  w.abs_off = w.partial_off + align256(n * sizeof(double));
+  w.wit_off = w.abs_off + align256(n * sizeof(double));
   w.rk_off = w.wit_off + align256(n * sizeof(uint32_t));
   w.bytes = w.rk_off + (nr ? align256(bh * padded_tokens(N) * sizeof(float)) : 0);
   return w;
 }
 
-// sage_quant_v workspace: arrival counters [BH] (as above), fp64 partial sums,
-// fp32 partial min and max, exactness witnesses [BH][nchunk][D], per-channel
-// 448/a [BH][D].
+// sage_quant_v workspace: arrival counters [BH] (as above), fp64 partial sums
+// and sums of |x|, fp32 partial min and max, exactness witnesses
+// [BH][nchunk][D], per-channel 448/a [BH][D].
 struct VWorkspace {
-  size_t cnt_off, sum_off, min_off, max_off, wit_off, inv_off, bytes;
+  size_t cnt_off, sum_off, abs_off, min_off, max_off, wit_off, inv_off, bytes;
 };
 inline VWorkspace v_workspace(int B, int N, int H, int D) {
   StatsSplit s = stats_split(B, N, H);
@@ -66,7 +67,8 @@ inline VWorkspace v_workspace(int B, int N, int H, int D) {
   VWorkspace w;
   w.cnt_off = 0;
   w.sum_off = kCounterBytes;
-  w.min_off = w.sum_off + align256(n * sizeof(double));
+  w.abs_off = w.sum_off + align256(n * sizeof(double));
+  w.min_off = w.abs_off + align256(n * sizeof(double));
   w.max_off = w.min_off + align256(n * sizeof(float));
   w.wit_off = w.max_off + align256(n * sizeof(float));
   w.inv_off = w.wit_off + align256(n * sizeof(uint32_t));

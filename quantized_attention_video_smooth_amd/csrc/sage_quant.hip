@@ -39,31 +39,31 @@ __device__ __forceinline__ int v_slot(int t) {
 // fp64(exact sum) / N rounded to fp32: the exact sum rounded once to fp64.
 // Plain fp64 accumulation (in any order) reaches that value whenever every
 // partial sum is representable: all values are multiples of the smallest ulp
-// u among the non-zero ones, so this holds when N * max|x| < 2^53 * u.  The
-// statistics pass records, per chunk and channel, max |x| and the smallest
-// non-zero |x| (as bf16 bit patterns, packed two channels per word with
-// 16-bit integer min / max); a channel that fails the test has its sum
-// recomputed exactly (ExactSum) by the head's finalisation.
+// u among the non-zero ones, and every partial sum is bounded by S = sum |x|,
+// so this holds when S < 2^53 * u.  S itself is accumulated in fp64 next to
+// the sum; a computed S below 2^52 * u proves the true S below 2^53 * u (a
+// sum of non-negative terms loses less than a relative N * 2^-53 to rounding).
+// The statistics pass records, per chunk and channel, S and the smallest
+// non-zero |x| (as a bf16 bit pattern, two channels per word, 16-bit integer
+// min); a channel that fails the test has its sum recomputed exactly
+// (ExactSum) by the head's finalisation, with the whole workgroup.
 // ---------------------------------------------------------------------------
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// Witness of 2 bf16 (one 32-bit word) folded into (wmax, wmin): wmax = max
-// |x| bits, wmin = min (|x| bits - 1) with 0 wrapping to 0xFFFF (no value).
-__device__ __forceinline__ void witness2(uint32_t w, uint32_t& wmax, uint32_t& wmin) {
-  const u16x2 a = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
-  const u16x2 am1 = a - (u16x2){1, 1};
-  wmax = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, wmax), a));
+// Witness of 2 bf16 (one 32-bit word) folded into wmin = min (|x| bits - 1),
+// with 0 wrapping to 0xFFFF (no non-zero value).
+__device__ __forceinline__ void witness2(uint32_t w, uint32_t& wmin) {
+  const u16x2 am1 = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu) - (u16x2){1, 1};
   wmin = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, wmin), am1));
 }
 
 // True when plain fp64 accumulation of the channel is exact in any order,
-// from its witness over N values (max bits, min non-zero bits - 1).
-__device__ __forceinline__ bool sum_is_exact(uint32_t mxb, uint32_t mnb, int N) {
+// from its witness (min non-zero |x| bits - 1) and its computed sum of |x|.
+__device__ __forceinline__ bool sum_is_exact(uint32_t mnb, double sum_abs) {
   if (mnb == 0xFFFFu) return true;  // every value is zero
   const uint32_t e = (mnb + 1) >> 7;  // biased exponent of the smallest non-zero |x|
   const int eu = (e == 0 ? 1 : (int)e) - 134;  // its ulp is 2^eu
-  const double mx = (double)__uint_as_float(mxb << 16);
-  return (double)N * mx < __builtin_ldexp(1.0, 53 + eu);
+  return sum_abs < __builtin_ldexp(1.0, 52 + eu);
 }
 
 // Exact sum of bf16 values: an integer in units of 2^-133 (the smallest bf16
@@ -165,6 +165,40 @@ struct ExactSum {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Hand-over of the per-chunk partials to the head's last workgroup.  The
+// workgroups of a head run on different XCDs, each behind its own L2, which
+// does not keep ordinary stores coherent with the other XCDs.  A device-scope
+// fence makes them so by writing back and invalidating the whole L2, and one
+// such fence per workgroup (~2000 per call) costs more than the statistics
+// pass itself.  Instead, everything one workgroup writes for another goes out
+// as a relaxed agent-scope atomic store (written through to the device's
+// coherence point) and is read back as a relaxed agent-scope atomic load;
+// waiting for the stores to complete (vmcnt) before the ticket is taken
+// orders them before it, as the release half of a fence would, without the
+// L2 write-back that only ordinary stores need.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_agent(double* p, double v) {
+  __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store((uint32_t*)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_agent(const double* p) {
+  return __builtin_bit_cast(double, __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __builtin_bit_cast(float, __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All of this wave's memory operations complete; also a compiler barrier.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Channel value of the QK RMSNorm + RoPE producer for token row x (bf16, unit
 // channel stride) at channel d, given the row's r: the arithmetic of
 // norm_rope_apply for the pair (d & ~1, d | 1), one channel returned.
@@ -191,12 +225,13 @@ __device__ __forceinline__ uint32_t nr_channel_bits(const uint16_t* xrow, int d,
 // Channel statistics + per-head finalisation: grid (nchunk, B*H), 256
 // threads.  Each thread owns 8 consecutive channels (one 16-byte load per
 // token row); D/8 threads cover a row, so a pass reads 256/(D/8) rows.  A
-// workgroup writes its chunk's partials (fp64 sums, V's min / max, the
-// exactness witnesses), then takes a ticket from the head's arrival counter;
-// the last of the head's nchunk workgroups reduces the partials in ascending
-// chunk order and writes the head's mean (K: k_mean = bf16(fp32(sum / N));
-// V: v_mean, v_scale and 448/a for the quantisation pass), recomputing the
-// sum exactly for a channel whose witness fails, and leaves the counter zero.
+// workgroup writes its chunk's partials (fp64 sums and sums of |x|, V's
+// min / max, the exactness witnesses), then takes a ticket from the head's
+// arrival counter; the last of the head's nchunk workgroups reduces the
+// partials in ascending chunk order and writes the head's mean (K: k_mean =
+// bf16(fp32(sum / N)); V: v_mean, v_scale and 448/a for the quantisation
+// pass), recomputing the sum exactly for a channel whose witness fails, and
+// leaves the counter zero.
 // ---------------------------------------------------------------------------
 // NR: the rows are first put through the QK RMSNorm + RoPE producer
 // (weights nr_w, table rope), so the statistics are those of the producer's
@@ -204,25 +239,25 @@ __device__ __forceinline__ uint32_t nr_channel_bits(const uint16_t* xrow, int d,
 template <int D, bool IS_V, bool NR = false>
 __global__ __launch_bounds__(kThreads) void stats_kernel(
     const uint16_t* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, int H, int N, int nchunk,
-    int rows_per_chunk, double* __restrict__ psum, float* __restrict__ pmin,
-    float* __restrict__ pmax, uint32_t* __restrict__ pwit, int* __restrict__ cnt,
-    const uint16_t* __restrict__ nr_w, const float* __restrict__ rope, double eps,
-    float* __restrict__ rk, int Np, uint16_t* __restrict__ k_mean, float* __restrict__ v_mean,
-    float* __restrict__ v_scale, float* __restrict__ v_inv) {
+    int rows_per_chunk, double* __restrict__ psum, double* __restrict__ pabs,
+    float* __restrict__ pmin, float* __restrict__ pmax, uint32_t* __restrict__ pwit,
+    int* __restrict__ cnt, const uint16_t* __restrict__ nr_w, const float* __restrict__ rope,
+    double eps, float* __restrict__ rk, int Np, uint16_t* __restrict__ k_mean,
+    float* __restrict__ v_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
-  constexpr int TPC = kThreads / D;  // threads per channel in the exact re-summation
-  // s_sum's storage is reused for the witnesses, then for the exact sums
+  // s_sum holds the per-row-group sums, then the sums of |x|, the witnesses
+  // and the exact sums' merge tree in turn
   __shared__ __attribute__((aligned(16))) double s_sum[RPP][D];
   __shared__ float s_min[IS_V ? RPP : 1][D];
   __shared__ float s_max[IS_V ? RPP : 1][D];
-  __shared__ int s_last;
-  __shared__ int s_flag[D];
-  static_assert(2 * sizeof(uint32_t) * RPP * (D / 2) <= sizeof(double) * RPP * D, "witness alias");
-  static_assert(sizeof(uint64_t) * 10 * (TPC - 1) * D <= sizeof(double) * RPP * D, "exact-sum alias");
-  uint32_t (*s_wmax)[D / 2] = (uint32_t(*)[D / 2])(&s_sum[0][0]);
-  uint32_t (*s_wmin)[D / 2] = s_wmax + RPP;
-  uint64_t (*s_ex)[D][10] = (uint64_t(*)[D][10])(&s_sum[0][0]);
+  __shared__ double s_xsum[D];  // exact sums of the flagged channels
+  __shared__ int s_list[D];     // the flagged channels
+  __shared__ int s_last, s_nflag;
+  static_assert(sizeof(uint32_t) * RPP * (D / 2) <= sizeof(double) * RPP * D, "witness alias");
+  static_assert(sizeof(uint64_t) * 10 * (kThreads / 2) <= sizeof(double) * RPP * D, "merge alias");
+  uint32_t (*s_wmin)[D / 2] = (uint32_t(*)[D / 2])(&s_sum[0][0]);
+  uint64_t (*s_ex)[10] = (uint64_t(*)[10])(&s_sum[0][0]);
 
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
@@ -232,22 +267,32 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   const int r0 = c * rows_per_chunk;
   const int r1 = min(N, r0 + rows_per_chunk);
 
-  double acc[8];
+  double acc[8], aacc[8];
   float mn[8], mx[8];
-  uint32_t wmax[4], wmin[4];
+  uint32_t wmin[4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     acc[j] = 0.0;
+    aacc[j] = 0.0;
     mn[j] = __builtin_inff();
     mx[j] = -__builtin_inff();
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    wmax[j] = 0;
-    wmin[j] = 0xFFFFFFFFu;
-  }
+  for (int j = 0; j < 4; ++j) wmin[j] = 0xFFFFFFFFu;
   float w8[8];
   if constexpr (NR) load_w8(nr_w, lc, w8);
+  auto fold = [&](const float (&f)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double d = (double)f[j];
+      acc[j] += d;
+      aacc[j] += __builtin_fabs(d);
+      if (IS_V) {
+        mn[j] = fminf(mn[j], f[j]);
+        mx[j] = fmaxf(mx[j], f[j]);
+      }
+    }
+  };
   // every lane of a token row takes the same path (the row index depends on
   // the row, not the lane), as the producer's cross-lane sum needs
   auto take = [&](const uint4& v, int row) {
@@ -260,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
       for (int j = 0; j < 8; ++j) f1[0][j] = f[j];
       load_cs8<D>(rope, row, lc, cs[0]);
       rows_rsqrt<LPR, 1>(f1, eps, r, r_own);
-      if (lc == 0) rk[(size_t)bh * Np + row] = r_own;
+      if (lc == 0) st_agent(rk + (size_t)bh * Np + row, r_own);
       norm_rope_apply<1>(f1, w8, cs, r);
 #pragma unroll
       for (int j = 0; j < 8; ++j) f[j] = f1[0][j];
@@ -268,15 +313,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
       for (int j = 0; j < 4; ++j) wd[j] = bf16x2_rne(f[2 * j], f[2 * j + 1]);  // exact: bf16 values
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) witness2(wd[j], wmax[j], wmin[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[j] += (double)f[j];
-      if (IS_V) {
-        mn[j] = fminf(mn[j], f[j]);
-        mx[j] = fmaxf(mx[j], f[j]);
-      }
-    }
+    for (int j = 0; j < 4; ++j) witness2(wd[j], wmin[j]);
+    fold(f);
   };
   int r = r0 + lr;
   if constexpr (!NR) {
@@ -303,19 +341,19 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
       for (int u = 0; u < 2; ++u) unpack8(v[u], f[u]);
       float rr[2], r_own;
       rows_rsqrt<LPR, 2>(f, eps, rr, r_own);
-      if ((lc & (LPR / 2 - 1)) == 0) rk[(size_t)bh * Np + r + (lc / (LPR / 2)) * RPP] = r_own;
+      if ((lc & (LPR / 2 - 1)) == 0) st_agent(rk + (size_t)bh * Np + r + (lc / (LPR / 2)) * RPP, r_own);
       norm_rope_apply<2>(f, w8, cs, rr);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) witness2(bf16x2_rne(f[u][2 * j], f[u][2 * j + 1]), wmax[j], wmin[j]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += (double)f[u][j];
+        for (int j = 0; j < 4; ++j) witness2(bf16x2_rne(f[u][2 * j], f[u][2 * j + 1]), wmin[j]);
+        fold(f[u]);
       }
     }
   }
   for (; r < r1; r += RPP) take(*(const uint4*)(base + (int64_t)r * sn), r);
 
+  // ---- chunk partials: row groups reduced in LDS in ascending order ----
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     s_sum[lr][lc * 8 + j] = acc[j];
@@ -325,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     }
   }
   __syncthreads();
-  double csum = 0.0;
+  double csum = 0.0, cabs = 0.0;
   float clo = __builtin_inff(), chi = -__builtin_inff();
   if (tid < D) {
     for (int i = 0; i < RPP; ++i) {
@@ -338,62 +376,65 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    s_wmax[lr][lc * 4 + j] = wmax[j];
-    s_wmin[lr][lc * 4 + j] = wmin[j];
-  }
+  for (int j = 0; j < 8; ++j) s_sum[lr][lc * 8 + j] = aacc[j];
+  __syncthreads();
+  if (tid < D)
+    for (int i = 0; i < RPP; ++i) cabs += s_sum[i][tid];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s_wmin[lr][lc * 4 + j] = wmin[j];
   __syncthreads();
   const size_t pbase = ((size_t)bh * nchunk + c) * D;
   if (tid < D) {
-    uint32_t wx = 0, wn = 0xFFFFu;
+    uint32_t wn = 0xFFFFu;
     const int sh16 = 16 * (tid & 1);
-    for (int i = 0; i < RPP; ++i) {
-      wx = max(wx, (s_wmax[i][tid >> 1] >> sh16) & 0xFFFFu);
-      wn = min(wn, (s_wmin[i][tid >> 1] >> sh16) & 0xFFFFu);
-    }
-    psum[pbase + tid] = csum;
+    for (int i = 0; i < RPP; ++i) wn = min(wn, (s_wmin[i][tid >> 1] >> sh16) & 0xFFFFu);
+    st_agent(psum + pbase + tid, csum);
+    st_agent(pabs + pbase + tid, cabs);
     if (IS_V) {
-      pmin[pbase + tid] = clo;
-      pmax[pbase + tid] = chi;
+      st_agent(pmin + pbase + tid, clo);
+      st_agent(pmax + pbase + tid, chi);
     }
-    pwit[pbase + tid] = (wx << 16) | wn;
+    st_agent(pwit + pbase + tid, wn);
   }
 
   // ---- arrival: the last workgroup of the head finalises it ----
-  __threadfence();  // this workgroup's partials before its ticket
+  wait_vm();  // this workgroup's partials (and r values) complete before its ticket
   __syncthreads();
   // (one chunk per head: every workgroup finalises its own head, no counter)
-  if (tid == 0) s_last = nchunk == 1 || atomicAdd(cnt + bh, 1) == nchunk - 1;
+  if (tid == 0)
+    s_last = nchunk == 1 ||
+             __hip_atomic_fetch_add(cnt + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nchunk - 1;
   __syncthreads();
-  if (!s_last) return;  // whole workgroup
-  __threadfence();      // every other workgroup's partials after the tickets
+  if (!s_last) return;  // whole workgroup; the partials below are read after the ticket
 
-  // Channels whose plain sum may be inexact: flagged in LDS, then summed
-  // exactly by all threads (channel d = tid % D, a stride of the tokens each).
-  double s_plain = 0.0;
+  double s_plain = 0.0, s_abs = 0.0;
   float lo = __builtin_inff(), hi = -__builtin_inff();
+  bool flagged = false;
   if (tid < D) {
     const size_t hb = (size_t)bh * nchunk * D + tid;
-    uint32_t wx = 0, wn = 0xFFFFu;
+    uint32_t wn = 0xFFFFu;
     int ch = 0;
     for (; ch + 8 <= nchunk; ch += 8) {  // 8 loads in flight, summed in ascending chunk order
-      double ps[8];
+      double ps[8], pa[8];
       float pl[8], ph[8];
       uint32_t pw[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        ps[u] = psum[hb + (size_t)(ch + u) * D];
-        pw[u] = pwit[hb + (size_t)(ch + u) * D];
+        const size_t o = hb + (size_t)(ch + u) * D;
+        ps[u] = ld_agent(psum + o);
+        pa[u] = ld_agent(pabs + o);
+        pw[u] = ld_agent(pwit + o);
         if (IS_V) {
-          pl[u] = pmin[hb + (size_t)(ch + u) * D];
-          ph[u] = pmax[hb + (size_t)(ch + u) * D];
+          pl[u] = ld_agent(pmin + o);
+          ph[u] = ld_agent(pmax + o);
         }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         s_plain += ps[u];
-        wx = max(wx, pw[u] >> 16);
-        wn = min(wn, pw[u] & 0xFFFFu);
+        s_abs += pa[u];
+        wn = min(wn, pw[u]);
         if (IS_V) {
           lo = fminf(lo, pl[u]);
           hi = fmaxf(hi, ph[u]);
@@ -401,60 +442,72 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
       }
     }
     for (; ch < nchunk; ++ch) {
-      s_plain += psum[hb + (size_t)ch * D];
-      const uint32_t pw = pwit[hb + (size_t)ch * D];
-      wx = max(wx, pw >> 16);
-      wn = min(wn, pw & 0xFFFFu);
+      const size_t o = hb + (size_t)ch * D;
+      s_plain += ld_agent(psum + o);
+      s_abs += ld_agent(pabs + o);
+      wn = min(wn, ld_agent(pwit + o));
       if (IS_V) {
-        lo = fminf(lo, pmin[hb + (size_t)ch * D]);
-        hi = fmaxf(hi, pmax[hb + (size_t)ch * D]);
+        lo = fminf(lo, ld_agent(pmin + o));
+        hi = fmaxf(hi, ld_agent(pmax + o));
       }
     }
-    s_flag[tid] = sum_is_exact(wx, wn, N) ? 0 : 1;
+    flagged = !sum_is_exact(wn, s_abs);
   }
+  // list of flagged channels (none for ordinary activations)
+  if (tid == 0) s_nflag = 0;
   __syncthreads();
-  // exact sums of the flagged channels (none for ordinary activations);
-  // part 0 keeps its sum in registers, parts 1.. hand theirs over in LDS
-  ExactSum ex;
-  ex.init();
-  {
-    const int d = tid % D, part = tid / D;
-    if (s_flag[d]) {
-      const uint16_t* col = head + d;
-      for (int n = part; n < N; n += TPC) {
-        uint32_t bits;
-        if constexpr (NR) {
-          const float* rope_row = rope + (size_t)n * D;  // (cos, sin) pairs: D floats per token
-          bits = nr_channel_bits<D>(head + (int64_t)n * sn, d, rk[(size_t)bh * Np + n], nr_w, rope_row);
-        } else {
-          bits = col[(int64_t)n * sn];
-        }
-        ex.add(bits);
+  if (tid < D && flagged) s_list[atomicAdd(&s_nflag, 1)] = tid;
+  __syncthreads();
+  const int nflag = s_nflag;
+  // Exact sum of each flagged channel by the whole workgroup: token n goes to
+  // thread n % 256, then the 256 partial sums are merged in a tree in LDS.
+  for (int i = 0; i < nflag; ++i) {
+    const int d = s_list[i];
+    ExactSum ex;
+    ex.init();
+    auto bits_at = [&](int n) -> uint32_t {
+      if constexpr (NR) {
+        const float* rope_row = rope + (size_t)n * D;  // (cos, sin) pairs: D floats per token
+        return nr_channel_bits<D>(head + (int64_t)n * sn, d, ld_agent(rk + (size_t)bh * Np + n), nr_w,
+                                  rope_row);
+      } else {
+        return head[(int64_t)n * sn + d];
       }
-      if (part > 0) {
+    };
+    int n = tid;
+    for (; n + 3 * kThreads < N; n += 4 * kThreads) {  // 4 loads in flight
+      uint32_t bv[4];
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          s_ex[part - 1][d][i] = ex.p[i];
-          s_ex[part - 1][d][5 + i] = ex.n[i];
+      for (int u = 0; u < 4; ++u) bv[u] = bits_at(n + u * kThreads);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ex.add(bv[u]);
+    }
+    for (; n < N; n += kThreads) ex.add(bits_at(n));
+    for (int w = kThreads / 2; w >= 1; w >>= 1) {
+      if (tid >= w && tid < 2 * w) {
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+          s_ex[tid - w][k] = ex.p[k];
+          s_ex[tid - w][5 + k] = ex.n[k];
         }
       }
-    }
-  }
-  __syncthreads();
-  if (tid < D) {
-    double s = s_plain;
-    if (s_flag[tid]) {
-      for (int part = 1; part < TPC; ++part) {
+      __syncthreads();
+      if (tid < w) {
         ExactSum o;
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          o.p[i] = s_ex[part - 1][tid][i];
-          o.n[i] = s_ex[part - 1][tid][5 + i];
+        for (int k = 0; k < 5; ++k) {
+          o.p[k] = s_ex[tid][k];
+          o.n[k] = s_ex[tid][5 + k];
         }
         ex.merge(o);
       }
-      s = ex.rounded();
+      __syncthreads();
     }
+    if (tid == 0) s_xsum[d] = ex.rounded();
+  }
+  __syncthreads();
+  if (tid < D) {
+    const double s = flagged ? s_xsum[tid] : s_plain;
     const float mean = (float)(s / (double)N);
     if (!IS_V) {
       k_mean[(size_t)bh * D + tid] = (uint16_t)bf16_bits_rne(mean);
@@ -467,7 +520,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
       v_inv[(size_t)bh * D + tid] = zero ? 0.0f : inv;
     }
   }
-  if (tid == 0 && nchunk > 1) cnt[bh] = 0;  // ready for the next call
+  if (tid == 0 && nchunk > 1)  // ready for the next call
+    __hip_atomic_store(cnt + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -808,7 +862,8 @@ hipError_t quant_qk_impl(const uint16_t* q, int64_t q_sb, int64_t q_sn, int64_t 
   float* rk = NR ? (float*)(wsb + w.rk_off) : nullptr;
   hipLaunchKernelGGL((stats_kernel<D, false, NR>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream,
                      k, k_sb, k_sn, k_sh, H, N, s.nchunk, s.rows_per_chunk,
-                     (double*)(wsb + w.partial_off), (float*)nullptr, (float*)nullptr,
+                     (double*)(wsb + w.partial_off), (double*)(wsb + w.abs_off), (float*)nullptr,
+                     (float*)nullptr,
                      (uint32_t*)(wsb + w.wit_off), (int*)(wsb + w.cnt_off), nr.wk, nr.rope, nr.eps, rk,
                      Np, k_mean, (float*)nullptr, (float*)nullptr, (float*)nullptr);
   hipError_t e = hipGetLastError();
@@ -831,7 +886,7 @@ hipError_t quant_v_impl(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t v
   float* inv = (float*)(wsb + w.inv_off);
   hipLaunchKernelGGL((stats_kernel<D, true>), dim3(s.nchunk, B * H), dim3(kThreads), 0, stream, v,
                      v_sb, v_sn, v_sh, H, N, s.nchunk, s.rows_per_chunk,
-                     (double*)(wsb + w.sum_off), (float*)(wsb + w.min_off),
+                     (double*)(wsb + w.sum_off), (double*)(wsb + w.abs_off), (float*)(wsb + w.min_off),
                      (float*)(wsb + w.max_off), (uint32_t*)(wsb + w.wit_off),
                      (int*)(wsb + w.cnt_off), (const uint16_t*)nullptr, (const float*)nullptr, 0.0,
                      (float*)nullptr, 0, (uint16_t*)nullptr, v_mean, v_scale, inv);

@@ -60,9 +60,9 @@ def test_static_scratch_matches_workspace_path(sage):
 
 
 def test_static_scratch_size_limit(sage):
-    # 20000 heads: one statistics chunk each, a 30 MB workspace > 8 MiB
+    # 20000 heads: one statistics chunk each, a 51 MB workspace > 16 MiB
     B, N, H, D = 1, 64, 20000, 128
-    assert sage.sage_quant_qk_workspace_size(B, N, H, D) > 8 << 20
+    assert sage.sage_quant_qk_workspace_size(B, N, H, D) > 16 << 20
     q = torch.zeros((B, N, H, D), dtype=torch.bfloat16, device="cuda")
     Np = 64
     outs = [torch.empty((B, H, Np, D), dtype=torch.int8, device="cuda"),

@@ -774,13 +774,13 @@ def measure_path(args, cfg, torch, synth, sage, streams):
         gbs = (work["quant_q_bytes"] + work["quant_k_bytes"]) / (avg["quant_qk"] * 1e-3) / 1e9
         gbs_v = work["quant_v_bytes"] / (avg["quant_v"] * 1e-3) / 1e9
         src = os.path.join(ROOT, "quantized_attention_video_smooth_amd", "csrc", "sage_quant.hip")
-        res["roofline"] = {"kernel": "sage_quant_qk (its statistics, finalisation and quantisation "
-                                     "kernels, one call)",
+        res["roofline"] = {"kernel": "sage_quant_qk (its statistics kernel, which also finalises "
+                                     "each head, and its quantisation kernel; one call)",
                            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": round(gbs / PEAK_HBM_GBS, 4),
                            "traffic": traffic_record(src, cfg.name, qb, kbl, kernel="quant_qk")}
-        res["roofline_quant_v"] = {"kernel": "sage_quant_v (its statistics, finalisation and quantisation "
-                                             "kernels, one call)",
+        res["roofline_quant_v"] = {"kernel": "sage_quant_v (its statistics kernel, which also finalises "
+                                             "each head, and its quantisation kernel; one call)",
                                    "bound": "hbm", "achieved": round(gbs_v, 1), "peak": PEAK_HBM_GBS,
                                    "unit": "GB/s", "frac": round(gbs_v / PEAK_HBM_GBS, 4),
                                    "traffic": traffic_record(src, cfg.name, qb, kbl, kernel="quant_v")}

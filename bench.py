@@ -549,8 +549,10 @@ def prewarm(run_step, torch, ms):
 
 def parse_variant(spec):
     """'opt=val[;opt=val...]' -> {opt: val} over the step options an ABBA
-    comparison may vary (streams, producer, q_block, k_block)."""
-    allowed = {"streams": int, "producer": str, "q_block": int, "k_block": int, "waves": int}
+    comparison may vary (streams, producer, q_block, k_block, attention
+    workgroup size and key-step schedule)."""
+    allowed = {"streams": int, "producer": str, "q_block": int, "k_block": int, "waves": int,
+               "sched": int}
     out = {}
     if spec in ("", "default"):
         return out
@@ -563,8 +565,9 @@ def parse_variant(spec):
     if out.get("producer", "none") not in ("none", "fused", "composed"):
         raise SystemExit("--abba: producer is none, fused or composed")
     if out.get("streams", 1) not in (1, 2) or out.get("q_block", 32) not in (1, 32) \
-            or out.get("k_block", 64) not in (16, 64) or out.get("waves", 0) not in (0, 4, 8):
-        raise SystemExit("--abba: streams 1|2, q_block 1|32, k_block 16|64, waves 0|4|8")
+            or out.get("k_block", 64) not in (16, 64) or out.get("waves", 0) not in (0, 4, 8) \
+            or out.get("sched", 0) not in (0, 1, 2):
+        raise SystemExit("--abba: streams 1|2, q_block 1|32, k_block 16|64, waves 0|4|8, sched 0|1|2")
     return out
 
 
@@ -607,7 +610,7 @@ class AttentionPath:
         self.ev_in = [torch.cuda.Event() for _ in range(2)]
         self.do_attn = cfg.name != "quant_long"
 
-    def step_fn(self, streams, producer, qb, kbl, waves=None):
+    def step_fn(self, streams, producer, qb, kbl, waves=None, sched=None):
         """The step for these options.  step(evs=None, main=None): evs maps a
         call name to its (start, end) events, recorded on the stream the call
         runs on; main is the step's stream (the capture stream under --graph).
@@ -646,6 +649,8 @@ class AttentionPath:
         def step(evs=None, main=None):
             if waves is not None:
                 lib.sage_attn_tuning(waves)
+            if sched is not None:
+                lib.sage_attn_schedule(sched)
             two = streams == 2
             stream_ = self.stream if main is None else main
             sp_ = int(stream_.cuda_stream)
@@ -805,7 +810,7 @@ def run_abba(args, cfg, torch, synth, sage):
     if len(specs) != 2:
         raise SystemExit("--abba takes two variants: A,B (each 'opt=val[;opt=val]' or 'default')")
     base = {"streams": args.streams, "producer": args.producer, "q_block": args.q_block,
-            "k_block": args.k_block, "waves": 0}
+            "k_block": args.k_block, "waves": 0, "sched": 0}
     var = []
     for s in specs:
         o = dict(base)
@@ -813,7 +818,8 @@ def run_abba(args, cfg, torch, synth, sage):
         var.append(o)
     need_prod = any(o["producer"] != "none" for o in var)
     path = AttentionPath(torch, synth, sage, cfg, args.seed, need_prod)
-    steps = [path.step_fn(o["streams"], o["producer"], o["q_block"], o["k_block"], o["waves"]) for o in var]
+    steps = [path.step_fn(o["streams"], o["producer"], o["q_block"], o["k_block"], o["waves"], o["sched"])
+             for o in var]
     key = "attn_fwd" if path.do_attn else "quant_qk"
 
     def block(step):
@@ -911,7 +917,7 @@ def main():
     ap.add_argument("--abba", default=None,
                     help="A,B: same-process ABBA comparison of two step variants on --workload, each "
                          "'opt=val[;opt=val]' over streams, producer, q_block, k_block, waves (attention "
-                         "workgroup size 0|4|8) (or 'default'); "
+                         "workgroup size 0|4|8), sched (attention key-step schedule 0|1|2) (or 'default'); "
                          "--steps steps per block, --abba-groups groups")
     ap.add_argument("--abba-groups", type=int, default=15)
     ap.add_argument("--copy-calibration", action="store_true",

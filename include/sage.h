@@ -394,6 +394,14 @@ int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
  * on it.  Returns SAGE_OK or SAGE_ERR_VALUE. */
 int sage_attn_tuning(int waves_per_workgroup);
 
+/* Benchmark hook (process-wide, like sage_attn_tuning): forces the
+ * instruction schedule of later sage_attn_fwd* launches: 0 the library's
+ * default, 1 the compiler's own order of each key step, 2 each step's MFMAs
+ * spread through its softmax instructions (the previous tile's P.V first).
+ * The output does not depend on it (the same operations on the same values).
+ * Returns SAGE_OK or SAGE_ERR_VALUE. */
+int sage_attn_schedule(int schedule);
+
 /* Host-only argument checks of the three entry points: same arguments (less
  * the stream), same status codes, no HIP calls; usable without a GPU. */
 int sage_validate_quant_qk(const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh,

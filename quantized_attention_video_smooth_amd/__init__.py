@@ -57,6 +57,7 @@ _SIGS = {
                                 _vp, _i64, _i64, _i64], _i32),
     "sage_attn_launch_shape": ([_i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "sage_attn_tuning": ([_i32], _i32),
+    "sage_attn_schedule": ([_i32], _i32),
     "sage_quant_qk_ex": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _vp], _i32),
     "sage_attn_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
@@ -175,6 +176,12 @@ def sage_attn_tuning(waves: int = 0) -> None:
     """Benchmark hook: forced attention workgroup size (0 automatic, 4 or 8
     waves), process-wide."""
     _check(lib().sage_attn_tuning(waves), "sage_attn_tuning")
+
+
+def sage_attn_schedule(schedule: int = 0) -> None:
+    """Benchmark hook: forced attention key-step schedule (0 default, 1 the
+    compiler's order, 2 MFMAs spread through the softmax), process-wide."""
+    _check(lib().sage_attn_schedule(schedule), "sage_attn_schedule")
 
 
 def sage_padded_tokens(n: int) -> int:

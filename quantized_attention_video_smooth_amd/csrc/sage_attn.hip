@@ -45,6 +45,13 @@ namespace sage {
 // per launch by attn_waves).
 static std::atomic<int> g_attn_waves{0};
 void set_attn_waves(int waves) { g_attn_waves.store(waves, std::memory_order_relaxed); }
+// Key-step schedule forced for benchmark comparisons (0 = the default).
+static std::atomic<int> g_attn_sched{0};
+void set_attn_schedule(int schedule) { g_attn_sched.store(schedule, std::memory_order_relaxed); }
+static int attn_schedule() {
+  const int s = g_attn_sched.load(std::memory_order_relaxed);
+  return s == 0 ? 0 : s - 1;  // 1: the compiler's order, 2: interleaved
+}
 
 namespace {
 
@@ -101,7 +108,12 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 }
 
 // KB: K quantisation block (64: one scale per key tile; 16: four per tile).
-template <int D, int NW, int KB>
+// SCH: instruction schedule of a key step.  0: the compiler's own order;
+// 1: O^T += V^T P^T of the previous tile is issued at the start of the step,
+// and the step's 12 MFMAs are spread through the softmax's vector
+// instructions (sched_group_barrier), so that one wave alone keeps the matrix
+// cores busy in the shadow of its VALU work.
+template <int D, int NW, int KB, int SCH>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 
   // Softmax of S^T(t) (in scur): row max, P = exp2(s*c - m) * 448 packed to
   // E4M3 (byte 16*kb + i of pop), row sum, accumulator rescale.
-  auto softmax = [&](int t, v16i (&scur)[2], auto masked_tag) __attribute__((always_inline)) {
+  auto softmax = [&](int t, v16i (&scur)[2], auto masked_tag, auto sched_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     // c[j]: score multiplier of K block j of the tile; with KB = 16, block j
     // holds keys 16j..16j+15 = registers 8*(j%2)..+8 of scur[j/2]
@@ -303,6 +315,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pop[4 * kb + r] = w;
       }
+    if constexpr (decltype(sched_tag)::value) {
+      // this block holds (in program order) the previous tile's 4 PV MFMAs,
+      // the 8 K-operand reads and 8 S^T MFMAs of the next tile, this tile's
+      // 8 V-operand reads and the softmax up to the rescale branch
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // K operand reads
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a PV MFMA (previous tile)
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an S^T MFMA (next tile)
+        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // V operand reads
+    }
     // Keep the exponentials and packs in this basic block, ahead of the
     // rescale branch (the compiler would sink them past it): there they
     // share a block with the next tile's S^T MFMAs, and the register
@@ -339,15 +368,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   // steady_tag: std::true_type when tile t+AHEAD is known to exist, so the
   // refill and its wait need no run-time condition (no branch merging in
   // front of the next step's operand reads and their waits).
-  auto step = [&](int t, int u, v16i (&scur)[2], v16i (&snext)[2], auto masked_tag, auto next_tag,
+  auto step = [&](int t, int u, v16i (&scur)[2], v16i (&snext)[2], v8i (&vcur)[C::DC],
+                  v8i (&vprev)[C::DC], auto masked_tag, auto next_tag,
                   auto steady_tag) __attribute__((always_inline)) {
     const bool issue = decltype(steady_tag)::value || t + C::AHEAD < ntiles;
+    if constexpr (SCH == 1) pv_mfma(vprev);  // previous tile (zero operands before tile 0)
     if (issue) gload_lds(t + C::AHEAD, (u + C::AHEAD) % C::NBUF);
     if constexpr (decltype(next_tag)::value) qk_mfma((u + 1) % C::NBUF, snext);
-    v8i vop[C::DC];
-    load_v(u, vop);
-    softmax(t, scur, masked_tag);
-    pv_mfma(vop);
+    load_v(u, vcur);
+    constexpr bool sched = SCH == 1 && decltype(next_tag)::value && decltype(steady_tag)::value &&
+                           !decltype(masked_tag)::value;
+    softmax(t, scur, masked_tag, std::integral_constant<bool, sched>{});
+    if constexpr (SCH == 0) pv_mfma(vcur);
     if (issue && C::AHEAD > 2) __builtin_amdgcn_s_waitcnt(kWaitLgkm0VmCpt<C::CPT>);
     else __builtin_amdgcn_s_waitcnt(kWaitAll);
     __asm__ volatile("s_barrier" ::: "memory");
@@ -361,6 +393,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   __syncthreads();
   v16i sA[2], sB[2];
   qk_mfma(0, sA);
+  // V^T operands of the even / odd tiles (SCH 1 multiplies the previous
+  // tile's at the start of each step: zero before tile 0 adds nothing)
+  v8i vA[C::DC], vB[C::DC];
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) vA[dc] = vB[dc] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
   // ---- key loop ----
   // Main loop: groups of four tiles followed by at least one more tile (all
@@ -375,31 +412,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   const std::false_type no{};
   const std::true_type yes{};
   for (; t + 3 + C::AHEAD < ntiles; t += 4) {  // every step of the group refills the ring
-    step(t, 0, sA, sB, no, yes, yes);
-    step(t + 1, 1, sB, sA, no, yes, yes);
-    step(t + 2, 2, sA, sB, no, yes, yes);
-    step(t + 3, 3, sB, sA, no, yes, yes);
+    step(t, 0, sA, sB, vA, vB, no, yes, yes);
+    step(t + 1, 1, sB, sA, vB, vA, no, yes, yes);
+    step(t + 2, 2, sA, sB, vA, vB, no, yes, yes);
+    step(t + 3, 3, sB, sA, vB, vA, no, yes, yes);
   }
   for (; t + 4 < ntiles; t += 4) {
-    step(t, 0, sA, sB, no, yes, no);
-    step(t + 1, 1, sB, sA, no, yes, no);
-    step(t + 2, 2, sA, sB, no, yes, no);
-    step(t + 3, 3, sB, sA, no, yes, no);
+    step(t, 0, sA, sB, vA, vB, no, yes, no);
+    step(t + 1, 1, sB, sA, vB, vA, no, yes, no);
+    step(t + 2, 2, sA, sB, vA, vB, no, yes, no);
+    step(t + 3, 3, sB, sA, vB, vA, no, yes, no);
   }
   for (; t + 2 < ntiles; t += 2) {
-    step(t, t % C::NBUF, sA, sB, no, yes, no);
-    step(t + 1, (t + 1) % C::NBUF, sB, sA, no, yes, no);
+    step(t, t % C::NBUF, sA, sB, vA, vB, no, yes, no);
+    step(t + 1, (t + 1) % C::NBUF, sB, sA, vB, vA, no, yes, no);
   }
-  auto last_step = [&](int t, v16i (&scur)[2], v16i (&snext)[2]) __attribute__((always_inline)) {
-    if (t < nfull) step(t, t % C::NBUF, scur, snext, no, no, no);
-    else step(t, t % C::NBUF, scur, snext, yes, no, no);
+  auto last_step = [&](int t, v16i (&scur)[2], v16i (&snext)[2], v8i (&vcur)[C::DC],
+                       v8i (&vprev)[C::DC]) __attribute__((always_inline)) {
+    if (t < nfull) step(t, t % C::NBUF, scur, snext, vcur, vprev, no, no, no);
+    else step(t, t % C::NBUF, scur, snext, vcur, vprev, yes, no, no);
+    if constexpr (SCH == 1) pv_mfma(vcur);  // the last tile's PV
   };
-  // t is even here: S^T(t) is in sA
+  // t is even here: S^T(t) is in sA, its V^T operands go to vA
   if (t + 1 < ntiles) {
-    step(t, t % C::NBUF, sA, sB, no, yes, no);
-    last_step(t + 1, sB, sA);
+    step(t, t % C::NBUF, sA, sB, vA, vB, no, yes, no);
+    last_step(t + 1, sB, sA, vB, vA);
   } else {
-    last_step(t, sA, sB);
+    last_step(t, sA, sB, vA, vB);
   }
 
   // ---- epilogue: O = acc / (448 * l) * v_scale + v_mean, bf16 NHD ----
@@ -426,7 +465,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   }
 }
 
-template <int D, int NW, int KB>
+template <int D, int NW, int KB, int SCH>
 hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                        const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                        const float* v_mean, int B, int Nq, int Nk, int H, int q_block,
@@ -438,7 +477,7 @@ hipError_t attn_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k
   const int total = B * H * n_qtiles;
   const int grid = (int)ceil_div(total, 8) * 8;
   const float cq0 = sm_scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, KB>), dim3(grid), dim3(C::NT), 0, stream, q_i8, q_scale,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, KB, SCH>), dim3(grid), dim3(C::NT), 0, stream, q_i8, q_scale,
                      k_i8, k_scale, v_fp8, v_scale, v_mean, H, Nq, Npq, Nk, Npk, n_qtiles, total,
                      q_block, cq0,
                      out, o_sb, o_sn, o_sh);
@@ -471,11 +510,13 @@ hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
                      const float* v_mean, int B, int Nq, int Nk, int H, int q_block,
                      float sm_scale, uint16_t* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
                      hipStream_t stream) {
-  if (attn_waves(B, Nq, H) == 8)
-    return attn_launch<D, 8, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H,
-                                 q_block, sm_scale, out, o_sb, o_sn, o_sh, stream);
-  return attn_launch<D, 4, KB>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H,
-                               q_block, sm_scale, out, o_sb, o_sn, o_sh, stream);
+#define SAGE_ATTN_LAUNCH(NWW, SCHH)                                                               \
+  attn_launch<D, NWW, KB, SCHH>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H, \
+                                q_block, sm_scale, out, o_sb, o_sn, o_sh, stream)
+  const bool interleaved = attn_schedule() == 1;
+  if (attn_waves(B, Nq, H) == 8) return interleaved ? SAGE_ATTN_LAUNCH(8, 1) : SAGE_ATTN_LAUNCH(8, 0);
+  return interleaved ? SAGE_ATTN_LAUNCH(4, 1) : SAGE_ATTN_LAUNCH(4, 0);
+#undef SAGE_ATTN_LAUNCH
 }
 
 }  // namespace

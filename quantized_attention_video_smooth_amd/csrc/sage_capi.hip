@@ -493,6 +493,12 @@ int sage_attn_launch_shape(int B, int N, int H, int D, int* waves_per_workgroup,
   return SAGE_OK;
 }
 
+int sage_attn_schedule(int schedule) {
+  if (schedule < 0 || schedule > 2) return SAGE_ERR_VALUE;
+  sage::set_attn_schedule(schedule);
+  return SAGE_OK;
+}
+
 int sage_attn_tuning(int waves_per_workgroup) {
   if (waves_per_workgroup != 0 && waves_per_workgroup != 4 && waves_per_workgroup != 8)
     return SAGE_ERR_VALUE;

@@ -115,6 +115,9 @@ hipError_t launch_quant_v(const uint16_t* v, int64_t v_sb, int64_t v_sn, int64_t
 // Forced attention workgroup size (0 automatic, 4 or 8 waves), process-wide,
 // for benchmark comparisons.
 void set_attn_waves(int waves);
+// Forced key-step schedule of the attention (0 default, 1 compiler order,
+// 2 interleaved), process-wide, for benchmark comparisons.
+void set_attn_schedule(int schedule);
 
 // Waves per workgroup and grid size of the attention launch for these sizes
 // (N: queries).

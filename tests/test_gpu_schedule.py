@@ -1,0 +1,55 @@
+"""The attention's two key-step schedules (the compiler's order, and the MFMAs
+spread through the softmax with the previous tile's P.V first) run the same
+operations on the same values, so their outputs must be bit-identical: for
+both workgroup sizes, both K block sizes, D 64 and 128, ragged and padded key
+counts.  Each schedule's distance from the oracle is covered by the parity
+tests, which run the default one."""
+import sys
+
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_attention_video_smooth_amd as s
+    s.lib()
+    return s
+
+
+@pytest.mark.parametrize("shape", [(1, 300, 3, 64), (1, 1000, 2, 128), (2, 777, 5, 128), (1, 4608, 6, 128)],
+                         ids=["N300-D64", "N1000-D128", "B2-N777", "N4608"])
+@pytest.mark.parametrize("k_block", [64, 16])
+@pytest.mark.parametrize("waves", [4, 8])
+def test_schedules_bit_identical(sage, shape, k_block, waves):
+    B, N, H, D = shape
+    cfg = synth.custom(B, N, H, D, tag=500)
+    _log(f"[schedule] B{B} N{N} H{H} D{D} k_block {k_block} waves {waves}")
+    q, k, v = (t.cuda() for t in synth.make_qkv(cfg))
+    qk = sage.quant_qk(q, k, k_block=k_block)
+    vq = sage.quant_v(v)
+    outs = []
+    try:
+        sage.sage_attn_tuning(waves)
+        for sched in (1, 2):
+            sage.sage_attn_schedule(sched)
+            outs.append(sage.attn_fwd(*qk[:4], *vq, N))
+        torch.cuda.synchronize()
+    finally:
+        sage.sage_attn_schedule(0)
+        sage.sage_attn_tuning(0)
+    a, b = (o.view(torch.int16) for o in outs)
+    _log(f"  differing outputs: {int((a != b).sum())} of {a.numel()}")
+    assert torch.isfinite(outs[0].float()).all()
+    assert torch.equal(a, b)

@@ -519,7 +519,7 @@ def run_sp_share(args, torch, synth, sage, cfg):
         "prewarm": pw,
         "kernels_ms": stat,
         "kernels_ms_source": "HIP events around each call inside the timed steps",
-        "roofline": {"kernel": f"sage_attn_fwd_shard (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave "
+        "roofline": {"kernel": f"sage_attn_fwd_shard (attn_fwd_kernel<{D}, {waves}, {kbl}, 0>: {waves}-wave "
                                f"workgroups, {wgs} per launch)",
                      "bound": "mfma", "achieved": round(at, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(at / PEAK_MFMA_TFLOPS, 4), "traffic": None},
@@ -761,7 +761,7 @@ def measure_path(args, cfg, torch, synth, sage, streams):
         res["value"] = round(work["attn_ops"] / step_s / 1e12, 3)
         res["unit"] = "TFLOPS"
         res["roofline"] = {
-            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}, {kbl}>: {waves}-wave workgroups, "
+            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}, {kbl}, 0>: {waves}-wave workgroups, "
                       f"{wgs} per launch)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),

@@ -11,15 +11,21 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t padded_tokens(int64_t N) { return ceil_div(N, 64) * 64; }
 
-// Token chunks per (b, h) for the channel-statistics pass: enough workgroups
-// to cover the 256 CUs several times, never a chunk shorter than 64 tokens.
+// Token chunks per (b, h) for the channel-statistics pass: about 1024
+// workgroups (four per CU of a 256-CU part, the occupancy the pass runs at),
+// never a chunk shorter than 64 tokens.  Same-box timings of 512, 1024, 2048
+// and 4096 target workgroups (sage_quant_qk / sage_quant_v per call): at the
+// quant-only size (B1 H40 N32760) 1024 was best, 512 2-4% slower; at the FLUX
+// joint size (B2 H24 N4608) 512 was best, 1024 7-9% slower and 2048 16-32%
+// slower.  More chunks add per-workgroup reduction and hand-over costs and a
+// longer finalisation; fewer leave HBM latency exposed on large inputs.
 struct StatsSplit {
   int nchunk;
   int rows_per_chunk;
 };
 inline StatsSplit stats_split(int B, int N, int H) {
   int64_t bh = (int64_t)B * H;
-  int64_t want = ceil_div(2048, bh);
+  int64_t want = ceil_div(1024, bh);
   int64_t maxc = ceil_div(N, 64);
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
@@ -29,7 +35,7 @@ inline StatsSplit stats_split(int B, int N, int H) {
 
 // Arrival counters at the start of every quantiser workspace: one int per
 // (b, h) when a head is split into more than one statistics chunk, which
-// happens only for fewer than 2048 heads (stats_split).  The region has a
+// happens only for fewer than 1024 heads (stats_split).  The region has a
 // fixed size, so partials of one shape never land on the counters of another;
 // it must be zero before a workspace's first use and every call leaves it zero.
 constexpr size_t kCounterBytes = 2048 * sizeof(int);

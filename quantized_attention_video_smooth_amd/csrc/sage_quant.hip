@@ -246,17 +246,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
     float* __restrict__ v_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
   constexpr int LPR = D / 8;
   constexpr int RPP = kThreads / LPR;
-  // s_sum holds the per-row-group sums, then the sums of |x|, the witnesses
-  // and the exact sums' merge tree in turn
+  // s_sum holds the waves' partials, then the finalisation's, then the exact
+  // sums' merge tree
   __shared__ __attribute__((aligned(16))) double s_sum[RPP][D];
   __shared__ float s_min[IS_V ? RPP : 1][D];
   __shared__ float s_max[IS_V ? RPP : 1][D];
   __shared__ double s_xsum[D];  // exact sums of the flagged channels
   __shared__ int s_list[D];     // the flagged channels
   __shared__ int s_last, s_nflag;
-  static_assert(sizeof(uint32_t) * RPP * (D / 2) <= sizeof(double) * RPP * D, "witness alias");
   static_assert(sizeof(uint64_t) * 10 * (kThreads / 2) <= sizeof(double) * RPP * D, "merge alias");
-  uint32_t (*s_wmin)[D / 2] = (uint32_t(*)[D / 2])(&s_sum[0][0]);
   uint64_t (*s_ex)[10] = (uint64_t(*)[10])(&s_sum[0][0]);
 
   const int c = blockIdx.x, bh = blockIdx.y;
@@ -325,6 +323,16 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) take(v[u], r + u * RPP);
     }
+    if (r < r1) {  // the leftover rows (fewer than 8 per thread) as one batch of loads
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = r + u * RPP < r1 ? *(const uint4*)(base + (int64_t)(r + u * RPP) * sn) : uint4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (r + u * RPP < r1) take(v[u], r + u * RPP);
+      r = r1;
+    }
   } else {
     // 2 rows per step, data and table loads issued together, the producer
     // run on both rows at once (2 rather than 4 rows: fewer live registers,
@@ -353,42 +361,63 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   }
   for (; r < r1; r += RPP) take(*(const uint4*)(base + (int64_t)r * sn), r);
 
-  // ---- chunk partials: row groups reduced in LDS in ascending order ----
+  // ---- chunk partials: the row groups of a wave combined by lane
+  // exchanges, then the waves' results in LDS (any order: the fp64 sums are
+  // exact whenever they are used) ----
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    s_sum[lr][lc * 8 + j] = acc[j];
-    if (IS_V) {
-      s_min[lr][lc * 8 + j] = mn[j];
-      s_max[lr][lc * 8 + j] = mx[j];
+  for (int m = LPR; m < 64; m *= 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] += __shfl_xor(acc[j], m);
+      aacc[j] += __shfl_xor(aacc[j], m);
+      if (IS_V) {
+        mn[j] = fminf(mn[j], __shfl_xor(mn[j], m));
+        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], m));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u16x2 o = __builtin_bit_cast(u16x2, (uint32_t)__shfl_xor((int)wmin[j], m));
+      wmin[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, wmin[j]), o));
     }
   }
+  constexpr int NWV = kThreads / 64;
+  double (*s_wsum)[D] = (double(*)[D])(&s_sum[0][0]);
+  double (*s_wabs)[D] = s_wsum + NWV;
+  uint32_t (*s_wwit)[D / 2] = (uint32_t(*)[D / 2])(s_wabs + NWV);
+  static_assert((2 * sizeof(double) * D + sizeof(uint32_t) * D / 2) * NWV <= sizeof(double) * RPP * D,
+                "wave partials alias");
+  const int wv = tid >> 6;
+  if ((tid & 63) < LPR) {  // the first row group of each wave holds the wave's values
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      s_wsum[wv][lc * 8 + j] = acc[j];
+      s_wabs[wv][lc * 8 + j] = aacc[j];
+      if (IS_V) {
+        s_min[wv][lc * 8 + j] = mn[j];
+        s_max[wv][lc * 8 + j] = mx[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_wwit[wv][lc * 4 + j] = wmin[j];
+  }
   __syncthreads();
-  double csum = 0.0, cabs = 0.0;
-  float clo = __builtin_inff(), chi = -__builtin_inff();
+  const size_t pbase = ((size_t)bh * nchunk + c) * D;
   if (tid < D) {
-    for (int i = 0; i < RPP; ++i) {
-      csum += s_sum[i][tid];
+    double csum = 0.0, cabs = 0.0;
+    float clo = __builtin_inff(), chi = -__builtin_inff();
+    uint32_t wn = 0xFFFFu;
+    const int sh16 = 16 * (tid & 1);
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      csum += s_wsum[i][tid];
+      cabs += s_wabs[i][tid];
+      wn = min(wn, (s_wwit[i][tid >> 1] >> sh16) & 0xFFFFu);
       if (IS_V) {
         clo = fminf(clo, s_min[i][tid]);
         chi = fmaxf(chi, s_max[i][tid]);
       }
     }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 8; ++j) s_sum[lr][lc * 8 + j] = aacc[j];
-  __syncthreads();
-  if (tid < D)
-    for (int i = 0; i < RPP; ++i) cabs += s_sum[i][tid];
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) s_wmin[lr][lc * 4 + j] = wmin[j];
-  __syncthreads();
-  const size_t pbase = ((size_t)bh * nchunk + c) * D;
-  if (tid < D) {
-    uint32_t wn = 0xFFFFu;
-    const int sh16 = 16 * (tid & 1);
-    for (int i = 0; i < RPP; ++i) wn = min(wn, (s_wmin[i][tid >> 1] >> sh16) & 0xFFFFu);
     st_agent(psum + pbase + tid, csum);
     st_agent(pabs + pbase + tid, cabs);
     if (IS_V) {
@@ -408,26 +437,37 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
   __syncthreads();
   if (!s_last) return;  // whole workgroup; the partials below are read after the ticket
 
+  // The head's partials: TPC threads per channel, each over every TPC-th
+  // batch of 8 chunks (8 loads of each kind in flight, masked at the end),
+  // their results combined in LDS.  Any order: the sums are exact whenever
+  // they are used (else the channel is summed again below).
+  constexpr int TPC = kThreads / D;
   double s_plain = 0.0, s_abs = 0.0;
   float lo = __builtin_inff(), hi = -__builtin_inff();
   bool flagged = false;
-  if (tid < D) {
-    const size_t hb = (size_t)bh * nchunk * D + tid;
+  {
+    const int d = tid % D, part = tid / D;
+    const size_t hb = (size_t)bh * nchunk * D + d;
     uint32_t wn = 0xFFFFu;
-    int ch = 0;
-    for (; ch + 8 <= nchunk; ch += 8) {  // 8 loads in flight, summed in ascending chunk order
+    for (int ch = 8 * part; ch < nchunk; ch += 8 * TPC) {
       double ps[8], pa[8];
       float pl[8], ph[8];
       uint32_t pw[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const size_t o = hb + (size_t)(ch + u) * D;
-        ps[u] = ld_agent(psum + o);
-        pa[u] = ld_agent(pabs + o);
-        pw[u] = ld_agent(pwit + o);
-        if (IS_V) {
-          pl[u] = ld_agent(pmin + o);
-          ph[u] = ld_agent(pmax + o);
+        ps[u] = pa[u] = 0.0;
+        pl[u] = __builtin_inff();
+        ph[u] = -__builtin_inff();
+        pw[u] = 0xFFFFu;
+        if (ch + u < nchunk) {
+          const size_t o = hb + (size_t)(ch + u) * D;
+          ps[u] = ld_agent(psum + o);
+          pa[u] = ld_agent(pabs + o);
+          pw[u] = ld_agent(pwit + o);
+          if (IS_V) {
+            pl[u] = ld_agent(pmin + o);
+            ph[u] = ld_agent(pmax + o);
+          }
         }
       }
 #pragma unroll
@@ -441,17 +481,37 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(
         }
       }
     }
-    for (; ch < nchunk; ++ch) {
-      const size_t o = hb + (size_t)ch * D;
-      s_plain += ld_agent(psum + o);
-      s_abs += ld_agent(pabs + o);
-      wn = min(wn, ld_agent(pwit + o));
-      if (IS_V) {
-        lo = fminf(lo, ld_agent(pmin + o));
-        hi = fmaxf(hi, ld_agent(pmax + o));
-      }
+    double (*s_psum)[D] = (double(*)[D])(&s_sum[0][0]);
+    double (*s_pabs)[D] = s_psum + TPC;
+    uint32_t (*s_pwit)[D] = (uint32_t(*)[D])(s_pabs + TPC);
+    static_assert((2 * sizeof(double) + sizeof(uint32_t)) * D * TPC <= sizeof(double) * RPP * D,
+                  "finalisation partials alias");
+    __syncthreads();  // the chunk partials' LDS is free again
+    s_psum[part][d] = s_plain;
+    s_pabs[part][d] = s_abs;
+    s_pwit[part][d] = wn;
+    if (IS_V) {
+      s_min[part][d] = lo;
+      s_max[part][d] = hi;
     }
-    flagged = !sum_is_exact(wn, s_abs);
+    __syncthreads();
+    if (tid < D) {
+      s_plain = s_abs = 0.0;
+      wn = 0xFFFFu;
+      lo = __builtin_inff();
+      hi = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < TPC; ++i) {
+        s_plain += s_psum[i][tid];
+        s_abs += s_pabs[i][tid];
+        wn = min(wn, s_pwit[i][tid]);
+        if (IS_V) {
+          lo = fminf(lo, s_min[i][tid]);
+          hi = fmaxf(hi, s_max[i][tid]);
+        }
+      }
+      flagged = !sum_is_exact(wn, s_abs);
+    }
   }
   // list of flagged channels (none for ordinary activations)
   if (tid == 0) s_nflag = 0;

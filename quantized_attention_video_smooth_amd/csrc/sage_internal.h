@@ -13,12 +13,14 @@ inline int64_t padded_tokens(int64_t N) { return ceil_div(N, 64) * 64; }
 
 // Token chunks per (b, h) for the channel-statistics pass: about 1024
 // workgroups (four per CU of a 256-CU part, the occupancy the pass runs at),
-// never a chunk shorter than 64 tokens.  Same-box timings of 512, 1024, 2048
-// and 4096 target workgroups (sage_quant_qk / sage_quant_v per call): at the
-// quant-only size (B1 H40 N32760) 1024 was best, 512 2-4% slower; at the FLUX
-// joint size (B2 H24 N4608) 512 was best, 1024 7-9% slower and 2048 16-32%
-// slower.  More chunks add per-workgroup reduction and hand-over costs and a
-// longer finalisation; fewer leave HBM latency exposed on large inputs.
+// but no chunk shorter than 384 tokens (or than N).  Same-box timings of 512,
+// 1024, 2048 and 4096 target workgroups (sage_quant_qk / sage_quant_v per
+// call): at the quant-only size (B1 H40 N32760: chunks of 1260 tokens at
+// 1024) 1024 was best, 512 2-4% slower; at the FLUX joint size (B2 H24 N4608)
+// 512 (chunks of 419 tokens) was best, 1024 (210 tokens) 7-9% slower and 2048
+// 16-32% slower.  A workgroup's partials, its hand-over and the head's
+// finalisation cost about as much as streaming ~400 tokens, so shorter chunks
+// lose; fewer workgroups than ~4 per CU leave HBM latency exposed.
 struct StatsSplit {
   int nchunk;
   int rows_per_chunk;
@@ -26,7 +28,7 @@ struct StatsSplit {
 inline StatsSplit stats_split(int B, int N, int H) {
   int64_t bh = (int64_t)B * H;
   int64_t want = ceil_div(1024, bh);
-  int64_t maxc = ceil_div(N, 64);
+  int64_t maxc = ceil_div(N, 384);
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
   int rpc = (int)ceil_div(N, want);

@@ -890,10 +890,11 @@ def main():
                          "otherwise; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--streams", type=int, choices=[1, 2], default=None,
-                    help="2 (default with attention): sage_quant_v runs on a second stream beside "
-                         "sage_quant_qk (they are independent); attention waits for both. 1 (default "
-                         "for quant_long, so each quantiser's event window is its own): in order")
+    ap.add_argument("--streams", type=int, choices=[1, 2], default=1,
+                    help="1 (default): the three calls in order on one stream, so each call's event "
+                         "window is its own. 2: sage_quant_v runs on a second stream beside "
+                         "sage_quant_qk (they are independent) and the attention waits for both "
+                         "(same-process ABBA: no faster at FLUX or Long T2V, 2%% slower at video early)")
     ap.add_argument("--q-block", type=int, choices=[32, 1], default=32,
                     help="Q scale granularity: one scale per 32-token block (default) or per token")
     ap.add_argument("--k-block", type=int, choices=[64, 16], default=64,
@@ -959,8 +960,6 @@ def main():
             raise SystemExit("--sp times the attention share: use an attention workload, no --producer")
         print(json.dumps(run_sp_share(args, torch, synth, sage, cfg)), flush=True)
         return
-    if args.streams is None:
-        args.streams = 1 if args.workload == "quant_long" else 2
     if args.abba:
         print(json.dumps(run_abba(args, cfg, torch, synth, sage)), flush=True)
         return

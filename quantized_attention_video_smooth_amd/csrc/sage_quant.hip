@@ -12,10 +12,10 @@
 // for the per-channel statistics (fp64 sums, and min / max for V) and once to
 // quantise.  The statistics pass splits every (b, h) into token chunks and
 // writes per-chunk partials; the last workgroup of each head to finish reduces
-// them in a fixed order and writes the head's mean (and V's scale).  The mean
-// is the exact channel sum rounded once to fp64, divided by N: fp64 sums of
-// bf16 values are exact in any order unless a channel mixes tiny and large
-// values, which the pass detects, and such a channel is summed again exactly.
+// them and writes the head's mean (and V's scale).  The mean is the exact
+// channel sum rounded once to fp64, divided by N: fp64 sums of bf16 values
+// are exact in any order unless a channel mixes tiny and large values, which
+// the pass detects, and such a channel is summed again exactly.
 #include <hip/hip_runtime.h>
 
 #include "sage_device.h"
@@ -228,10 +228,10 @@ __device__ __forceinline__ uint32_t nr_channel_bits(const uint16_t* xrow, int d,
 // workgroup writes its chunk's partials (fp64 sums and sums of |x|, V's
 // min / max, the exactness witnesses), then takes a ticket from the head's
 // arrival counter; the last of the head's nchunk workgroups reduces the
-// partials in ascending chunk order and writes the head's mean (K: k_mean =
-// bf16(fp32(sum / N)); V: v_mean, v_scale and 448/a for the quantisation
-// pass), recomputing the sum exactly for a channel whose witness fails, and
-// leaves the counter zero.
+// partials (in any order: the sums are exact whenever they are used) and
+// writes the head's mean (K: k_mean = bf16(fp32(sum / N)); V: v_mean, v_scale
+// and 448/a for the quantisation pass), recomputing the sum exactly for a
+// channel whose witness fails, and leaves the counter zero.
 // ---------------------------------------------------------------------------
 // NR: the rows are first put through the QK RMSNorm + RoPE producer
 // (weights nr_w, table rope), so the statistics are those of the producer's

@@ -10,7 +10,8 @@ FLUX.3 Action joint block, B2 H24 N4608 D128).  Prints ONE JSON line.
 quantisation kernels are inside the step).  A default run also measures the
 metric's other two parts in the same process and reports them under `parts`:
 attention on the long text-to-video shape (B1 H40 N32760 D128) and the
-quantisers' HBM GB/s on the quant-only shape of the same size.  Each workload
+quantisers' HBM GB/s on the quant-only shape of the same size; and, for
+reference, the video-early block (B2 H24 N3128 D128).  Each workload
 first runs back-to-back steps for --prewarm-ms (the GPU clock ramps up over
 the first tens of ms of load), then --warmup counted steps.  Per-kernel times
 come from HIP events recorded on the stream the kernels run on.
@@ -870,7 +871,7 @@ def run_abba(args, cfg, torch, synth, sage):
 
 # The metric's other parts, measured after the main workload in a default run
 # (attention at N = 32760, quantiser GB/s on the quant-only shape).
-DEFAULT_PARTS = ("long_t2v", "quant_long")
+DEFAULT_PARTS = ("video_early", "long_t2v", "quant_long")
 
 
 def main():
@@ -886,7 +887,7 @@ def main():
                     choices=["tiny", "flux_joint", "video_early", "long_t2v", "quant_long", "vmlp_proj"])
     ap.add_argument("--parts", default=None,
                     help="comma-separated further workloads measured in the same run and reported under "
-                         "'parts' (default: long_t2v,quant_long when the workload is flux_joint, none "
+                         "'parts' (default: video_early,long_t2v,quant_long when the workload is flux_joint, none "
                          "otherwise; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)

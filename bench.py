@@ -553,7 +553,7 @@ def parse_variant(spec):
     comparison may vary (streams, producer, q_block, k_block, attention
     workgroup size and key-step schedule)."""
     allowed = {"streams": int, "producer": str, "q_block": int, "k_block": int, "waves": int,
-               "sched": int}
+               "sched": int, "events": str}
     out = {}
     if spec in ("", "default"):
         return out
@@ -565,6 +565,8 @@ def parse_variant(spec):
         out[key] = allowed[key](val.strip())
     if out.get("producer", "none") not in ("none", "fused", "composed"):
         raise SystemExit("--abba: producer is none, fused or composed")
+    if out.get("events", "roofline") not in ("roofline", "all"):
+        raise SystemExit("--abba: events is roofline (the timed call only) or all (every call)")
     if out.get("streams", 1) not in (1, 2) or out.get("q_block", 32) not in (1, 32) \
             or out.get("k_block", 64) not in (16, 64) or out.get("waves", 0) not in (0, 4, 8) \
             or out.get("sched", 0) not in (0, 1, 2):
@@ -735,15 +737,32 @@ def measure_path(args, cfg, torch, synth, sage, streams):
         kernels_src = (f"HIP events around {timed[0]} inside the timed steps (event-record nodes of the "
                        "replayed graph, on the call's stream)")
     else:
+        # Only the roofline's calls are bracketed inside the timed steps: each
+        # recorded event adds a dependency gap of several us to the stream
+        # (FLUX step 411 us without events, 417 with them around the attention,
+        # 433 around all three calls).  With attention, the quantisers' per-call
+        # times come from as many further steps with events around every call.
+        timed = ["attn_fwd"] if do_attn else names
         evs_all = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    for k2 in names} for _ in range(args.steps)]
+                    for k2 in timed} for _ in range(args.steps)]
         torch.cuda.synchronize()
         t_start.record(stream)
         for i in range(args.steps):
             step(evs_all[i])
         t_end.record(stream)
         torch.cuda.synchronize()
-        kernels_src = "HIP events around each call inside the timed steps, on the call's stream"
+        kernels_src = ("HIP events around " + ", ".join(timed) + " inside the timed steps, on the call's "
+                       "stream")
+        if do_attn:
+            evs_more = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                         for k2 in ("quant_qk", "quant_v")} for _ in range(args.steps)]
+            for i in range(args.steps):
+                step(evs_more[i])
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                evs_all[i].update(evs_more[i])
+            kernels_src += ("; quant_qk and quant_v from as many further steps with events around every "
+                            "call")
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     per = {k2: [e[k2][0].elapsed_time(e[k2][1]) for e in evs_all] for k2 in evs_all[0]}
     kstats = {k2: _stats(v2) for k2, v2 in per.items()}
@@ -811,7 +830,7 @@ def run_abba(args, cfg, torch, synth, sage):
     if len(specs) != 2:
         raise SystemExit("--abba takes two variants: A,B (each 'opt=val[;opt=val]' or 'default')")
     base = {"streams": args.streams, "producer": args.producer, "q_block": args.q_block,
-            "k_block": args.k_block, "waves": 0, "sched": 0}
+            "k_block": args.k_block, "waves": 0, "sched": 0, "events": "roofline"}
     var = []
     for s in specs:
         o = dict(base)
@@ -822,10 +841,13 @@ def run_abba(args, cfg, torch, synth, sage):
     steps = [path.step_fn(o["streams"], o["producer"], o["q_block"], o["k_block"], o["waves"], o["sched"])
              for o in var]
     key = "attn_fwd" if path.do_attn else "quant_qk"
+    every = ["quant_qk", "quant_v"] + (["attn_fwd"] if path.do_attn else [])
 
-    def block(step):
-        evs = [{key: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))}
-               for _ in range(args.steps)]
+    def block(step, events):
+        # events "all": every call bracketed, as the timed steps once were
+        names = every if events == "all" else [key]
+        evs = [{k2: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for k2 in names} for _ in range(args.steps)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(path.stream)
         for i in range(args.steps):
@@ -842,7 +864,8 @@ def run_abba(args, cfg, torch, synth, sage):
     torch.cuda.synchronize()
     groups = []
     for _ in range(args.abba_groups):
-        a1, b1, b2, a2 = block(steps[0]), block(steps[1]), block(steps[1]), block(steps[0])
+        ea, eb = var[0]["events"], var[1]["events"]
+        a1, b1, b2, a2 = block(steps[0], ea), block(steps[1], eb), block(steps[1], eb), block(steps[0], ea)
         ga = ((a1[0] + a2[0]) / 2, (a1[1] + a2[1]) / 2)
         gb = ((b1[0] + b2[0]) / 2, (b1[1] + b2[1]) / 2)
         groups.append({"A_step_ms": round(ga[0], 5), "B_step_ms": round(gb[0], 5),
@@ -919,7 +942,8 @@ def main():
     ap.add_argument("--abba", default=None,
                     help="A,B: same-process ABBA comparison of two step variants on --workload, each "
                          "'opt=val[;opt=val]' over streams, producer, q_block, k_block, waves (attention "
-                         "workgroup size 0|4|8), sched (attention key-step schedule 0|1|2) (or 'default'); "
+                         "workgroup size 0|4|8), sched (attention key-step schedule 0|1|2), events "
+                         "(roofline|all: which calls the timed steps bracket with events) (or 'default'); "
                          "--steps steps per block, --abba-groups groups")
     ap.add_argument("--abba-groups", type=int, default=15)
     ap.add_argument("--copy-calibration", action="store_true",

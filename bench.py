@@ -551,9 +551,9 @@ def prewarm(run_step, torch, ms):
 def parse_variant(spec):
     """'opt=val[;opt=val...]' -> {opt: val} over the step options an ABBA
     comparison may vary (streams, producer, q_block, k_block, attention
-    workgroup size and key-step schedule)."""
+    workgroup size and key-step schedule, quantiser calls per step)."""
     allowed = {"streams": int, "producer": str, "q_block": int, "k_block": int, "waves": int,
-               "sched": int, "events": str}
+               "sched": int, "events": str, "qgroups": int}
     out = {}
     if spec in ("", "default"):
         return out
@@ -569,8 +569,9 @@ def parse_variant(spec):
         raise SystemExit("--abba: events is roofline (the timed call only) or all (every call)")
     if out.get("streams", 1) not in (1, 2) or out.get("q_block", 32) not in (1, 32) \
             or out.get("k_block", 64) not in (16, 64) or out.get("waves", 0) not in (0, 4, 8) \
-            or out.get("sched", 0) not in (0, 1, 2):
-        raise SystemExit("--abba: streams 1|2, q_block 1|32, k_block 16|64, waves 0|4|8, sched 0|1|2")
+            or out.get("sched", 0) not in (0, 1, 2) or not 1 <= out.get("qgroups", 1) <= 40:
+        raise SystemExit("--abba: streams 1|2, q_block 1|32, k_block 16|64, waves 0|4|8, sched 0|1|2, "
+                         "qgroups 1..40")
     return out
 
 
@@ -613,12 +614,15 @@ class AttentionPath:
         self.ev_in = [torch.cuda.Event() for _ in range(2)]
         self.do_attn = cfg.name != "quant_long"
 
-    def step_fn(self, streams, producer, qb, kbl, waves=None, sched=None):
+    def step_fn(self, streams, producer, qb, kbl, waves=None, sched=None, qgroups=1):
         """The step for these options.  step(evs=None, main=None): evs maps a
         call name to its (start, end) events, recorded on the stream the call
         runs on; main is the step's stream (the capture stream under --graph).
         With streams == 2, sage_quant_v runs on a side stream beside the Q/K
-        segment and the attention waits for both."""
+        segment and the attention waits for both.  qgroups > 1 (B = 1 only)
+        runs each quantiser as that many calls over consecutive head groups,
+        each call's statistics pass followed by its quantisation: the second
+        read of a group's K or V then follows its first closely."""
         lib, cfg = self.lib, self.cfg
         B, N, H, D = cfg.B, cfg.N, cfg.H, cfg.D
         q, k, v, out = self.q, self.k, self.v, self.out
@@ -629,8 +633,27 @@ class AttentionPath:
               self.k_mean.data_ptr())
         pv = (self.v_fp8.data_ptr(), self.v_scale.data_ptr(), self.v_mean.data_ptr())
         ws_qk, ws_v = self.ws_qk, self.ws_v
+        if qgroups > 1 and (B != 1 or producer != "none" or qgroups > H):
+            raise SystemExit("qgroups > 1 needs B = 1, no producer and at most H groups")
+        hg = [(H * g // qgroups, H * (g + 1) // qgroups) for g in range(qgroups)]
+        Np = self.sage.sage_padded_tokens(N)
+
+        def heads(h0):
+            """Pointer offsets of head h0 (B = 1): inputs by their head stride,
+            outputs head-major and contiguous."""
+            return ((q.data_ptr() + 2 * h0 * qs[2], k.data_ptr() + 2 * h0 * ks[2], v.data_ptr() + 2 * h0 * vs[2]),
+                    (pq[0] + h0 * Np * D, pq[1] + 4 * h0 * (Np // qb), pq[2] + h0 * Np * D,
+                     pq[3] + 4 * h0 * (Np // kbl), pq[4] + 2 * h0 * D),
+                    (pv[0] + h0 * D * Np, pv[1] + 4 * h0 * D, pv[2] + 4 * h0 * D))
 
         def qk_call(sp_):
+            if qgroups > 1:
+                st_ = 0
+                for h0, h1 in hg:
+                    (pq_in, pk_in, _), pq_out, _ = heads(h0)
+                    st_ |= lib.sage_quant_qk_ex(pq_in, *qs, pk_in, *ks, B, N, h1 - h0, D, *pq_out,
+                                                ws_qk.data_ptr(), ws_qk.numel(), qb, kbl, sp_)
+                return st_
             if producer == "fused":
                 return lib.sage_norm_rope_quant_qk(
                     q.data_ptr(), *qs, k.data_ptr(), *ks, B, N, H, D, self.wq.data_ptr(), self.wk.data_ptr(),
@@ -671,7 +694,9 @@ class AttentionPath:
             st |= qk_call(sp_)
             rec("quant_qk", 1, stream_)
             rec("quant_v", 0, vs_)
-            st |= lib.sage_quant_v(v.data_ptr(), *vs, B, N, H, D, *pv, ws_v.data_ptr(), ws_v.numel(), vp_)
+            for h0, h1 in hg:
+                (_, _, pv_in), _, pv_out = heads(h0)
+                st |= lib.sage_quant_v(pv_in, *vs, B, N, h1 - h0, D, *pv_out, ws_v.data_ptr(), ws_v.numel(), vp_)
             rec("quant_v", 1, vs_)
             if two:
                 ev_in[1].record(side)
@@ -830,7 +855,7 @@ def run_abba(args, cfg, torch, synth, sage):
     if len(specs) != 2:
         raise SystemExit("--abba takes two variants: A,B (each 'opt=val[;opt=val]' or 'default')")
     base = {"streams": args.streams, "producer": args.producer, "q_block": args.q_block,
-            "k_block": args.k_block, "waves": 0, "sched": 0, "events": "roofline"}
+            "k_block": args.k_block, "waves": 0, "sched": 0, "events": "roofline", "qgroups": 1}
     var = []
     for s in specs:
         o = dict(base)
@@ -838,8 +863,8 @@ def run_abba(args, cfg, torch, synth, sage):
         var.append(o)
     need_prod = any(o["producer"] != "none" for o in var)
     path = AttentionPath(torch, synth, sage, cfg, args.seed, need_prod)
-    steps = [path.step_fn(o["streams"], o["producer"], o["q_block"], o["k_block"], o["waves"], o["sched"])
-             for o in var]
+    steps = [path.step_fn(o["streams"], o["producer"], o["q_block"], o["k_block"], o["waves"], o["sched"],
+                          o["qgroups"]) for o in var]
     key = "attn_fwd" if path.do_attn else "quant_qk"
     every = ["quant_qk", "quant_v"] + (["attn_fwd"] if path.do_attn else [])
 
@@ -943,7 +968,8 @@ def main():
                     help="A,B: same-process ABBA comparison of two step variants on --workload, each "
                          "'opt=val[;opt=val]' over streams, producer, q_block, k_block, waves (attention "
                          "workgroup size 0|4|8), sched (attention key-step schedule 0|1|2), events "
-                         "(roofline|all: which calls the timed steps bracket with events) (or 'default'); "
+                         "(roofline|all: which calls the timed steps bracket with events), qgroups (B = 1: "
+                         "each quantiser as that many calls over head groups) (or 'default'); "
                          "--steps steps per block, --abba-groups groups")
     ap.add_argument("--abba-groups", type=int, default=15)
     ap.add_argument("--copy-calibration", action="store_true",

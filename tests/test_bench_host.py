@@ -75,7 +75,8 @@ def test_abba_variant_parsing():
     assert bench.parse_variant("default") == {}
     assert bench.parse_variant("producer=fused;streams=1") == {"producer": "fused", "streams": 1}
     assert bench.parse_variant("q-block=1;k_block=16") == {"q_block": 1, "k_block": 16}
+    assert bench.parse_variant("qgroups=4") == {"qgroups": 4}
     import pytest
-    for bad in ("waves=3", "producer=both", "streams=3", "k_block=32", "q_block"):
+    for bad in ("waves=3", "producer=both", "streams=3", "k_block=32", "q_block", "qgroups=0", "qgroups=41"):
         with pytest.raises(SystemExit):
             bench.parse_variant(bad)

@@ -520,8 +520,8 @@ def run_sp_share(args, torch, synth, sage, cfg):
         "prewarm": pw,
         "kernels_ms": stat,
         "kernels_ms_source": "HIP events around each call inside the timed steps",
-        "roofline": {"kernel": f"sage_attn_fwd_shard (attn_fwd_kernel<{D}, {waves}, {kbl}, 0>: {waves}-wave "
-                               f"workgroups, {wgs} per launch)",
+        "roofline": {"kernel": f"sage_attn_fwd_shard (attn_fwd_kernel<{D}, {waves}, {kbl}, {attn_sch(waves)}>: "
+                               f"{waves}-wave workgroups, {wgs} per launch)",
                      "bound": "mfma", "achieved": round(at, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(at / PEAK_MFMA_TFLOPS, 4), "traffic": None},
     }
@@ -546,6 +546,13 @@ def prewarm(run_step, torch, ms):
         el = (time.perf_counter() - t0) * 1e3
         if el >= ms:
             return {"ms": round(el, 1), "steps": n}
+
+
+def attn_sch(waves, schedule=0):
+    """The attention kernel's schedule template argument for a launch of this
+    workgroup size under sage_attn_schedule(schedule): by default interleaved
+    (1) for four-wave workgroups, the compiler's order (0) for eight-wave ones."""
+    return {0: 1 if waves == 4 else 0, 1: 0, 2: 1}[schedule]
 
 
 def parse_variant(spec):
@@ -806,8 +813,8 @@ def measure_path(args, cfg, torch, synth, sage, streams):
         res["value"] = round(work["attn_ops"] / step_s / 1e12, 3)
         res["unit"] = "TFLOPS"
         res["roofline"] = {
-            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}, {kbl}, 0>: {waves}-wave workgroups, "
-                      f"{wgs} per launch)",
+            "kernel": f"sage_attn_fwd (attn_fwd_kernel<{D}, {waves}, {kbl}, {attn_sch(waves)}>: {waves}-wave "
+                      f"workgroups, {wgs} per launch)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_MFMA_TFLOPS,

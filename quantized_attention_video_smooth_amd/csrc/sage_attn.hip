@@ -28,7 +28,9 @@
 //     makes those bytes line up (sage_v_slot in sage.h);
 //   * software pipelining: S^T of tile t+1 is issued to the matrix cores before
 //     the softmax of tile t runs on the vector ALU, so the two overlap within
-//     a wave and across the two waves that share each SIMD;
+//     a wave and across the two waves that share each SIMD; four-wave
+//     workgroups also defer the P.V of tile t to the next step and spread all
+//     12 MFMAs of a step through its softmax instructions;
 //   * exp2 with log2(e) and the static P scale 448 folded into one FMA; the
 //     accumulator rescale is skipped when no row max moved.
 #include <hip/hip_runtime.h>
@@ -48,10 +50,9 @@ void set_attn_waves(int waves) { g_attn_waves.store(waves, std::memory_order_rel
 // Key-step schedule forced for benchmark comparisons (0 = the default).
 static std::atomic<int> g_attn_sched{0};
 void set_attn_schedule(int schedule) { g_attn_sched.store(schedule, std::memory_order_relaxed); }
-static int attn_schedule() {
-  const int s = g_attn_sched.load(std::memory_order_relaxed);
-  return s == 0 ? 0 : s - 1;  // 1: the compiler's order, 2: interleaved
-}
+// -1: the default (chosen by workgroup size), 0: the compiler's order,
+// 1: interleaved
+static int attn_schedule() { return g_attn_sched.load(std::memory_order_relaxed) - 1; }
 
 namespace {
 
@@ -109,10 +110,14 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 
 // KB: K quantisation block (64: one scale per key tile; 16: four per tile).
 // SCH: instruction schedule of a key step.  0: the compiler's own order;
-// 1: O^T += V^T P^T of the previous tile is issued at the start of the step,
-// and the step's 12 MFMAs are spread through the softmax's vector
-// instructions (sched_group_barrier), so that one wave alone keeps the matrix
-// cores busy in the shadow of its VALU work.
+// 1: in the steady main loop, O^T += V^T P^T of the previous tile is issued at
+// the start of the step, and the step's 12 MFMAs are spread through the
+// softmax's vector instructions (sched_group_barrier), so that one wave alone
+// keeps the matrix cores busy in the shadow of its VALU work.  Schedule 1
+// keeps the ring two tiles ahead, so the previous tile's slot is still intact
+// during the step and its V^T operands are read there again instead of being
+// held in registers.  Both schedules perform the same operations on the same
+// values in the same order per accumulator, so their outputs are identical.
 template <int D, int NW, int KB, int SCH>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
@@ -122,6 +127,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
     int total_tiles,
     int q_block, float cq0, uint16_t* __restrict__ out, int64_t o_sb, int64_t o_sn, int64_t o_sh) {
   using C = AttnCfg<D, NW>;
+  // tiles loaded ahead of the one in softmax (schedule 1 reads the slot of the
+  // previous tile during a step, so at most NBUF - 2 ahead)
+  constexpr int AHEAD = SCH == 1 ? 2 : C::AHEAD;
+  static_assert(SCH != 1 || AHEAD + 2 <= C::NBUF, "schedule 1 re-reads the previous tile's slot");
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NBUF * C::STAGE];
 
   // XCD-aware mapping: workgroup i runs on XCD i % 8; give each XCD a
@@ -316,21 +325,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
         pop[4 * kb + r] = w;
       }
     if constexpr (decltype(sched_tag)::value) {
-      // this block holds (in program order) the previous tile's 4 PV MFMAs,
-      // the 8 K-operand reads and 8 S^T MFMAs of the next tile, this tile's
-      // 8 V-operand reads and the softmax up to the rescale branch
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // K operand reads
+      // this block holds (in program order) the previous tile's 8 V-operand
+      // reads and 4 PV MFMAs, the 8 K-operand reads and 8 S^T MFMAs of the
+      // next tile and the softmax up to the rescale branch
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // V operand reads (previous tile)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a PV MFMA (previous tile)
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two K operand reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an S^T MFMA (next tile)
-        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // V operand reads
     }
     // Keep the exponentials and packs in this basic block, ahead of the
     // rescale branch (the compiler would sink them past it): there they
@@ -354,7 +363,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   };
 
   // One tile: start the direct loads of tile t+AHEAD into the ring slot of
-  // tile t-1 (whose last read, its V, was before the previous barrier), issue
+  // tile t+AHEAD-NBUF (t-1 or t-2, whose last reads were before the previous
+  // barrier; a deferred PV reads the slot of t-1 during the step), issue
   // S^T(t+1) on the matrix cores, run the softmax of tile t on the vector ALU
   // meanwhile, then O^T += V^T(t) P^T(t).  The closing barrier needs this
   // wave's LDS reads drained (the slot of tile t is refilled next step) and the
@@ -371,30 +381,42 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   auto step = [&](int t, int u, v16i (&scur)[2], v16i (&snext)[2], v8i (&vcur)[C::DC],
                   v8i (&vprev)[C::DC], auto masked_tag, auto next_tag,
                   auto steady_tag) __attribute__((always_inline)) {
-    const bool issue = decltype(steady_tag)::value || t + C::AHEAD < ntiles;
-    if constexpr (SCH == 1) pv_mfma(vprev);  // previous tile (zero operands before tile 0)
-    if (issue) gload_lds(t + C::AHEAD, (u + C::AHEAD) % C::NBUF);
+    const bool issue = decltype(steady_tag)::value || t + AHEAD < ntiles;
+    // schedule 1 defers the PV of a tile to the next step in the steady main
+    // loop only; the steps after it multiply their own tile's PV (after one
+    // flush), which keeps the register allocation of that code spill-free
+    constexpr bool deferred = SCH == 1 && decltype(steady_tag)::value;
+    if constexpr (deferred) {
+      // the previous tile, from its slot (zero V^T before tile 0: adds nothing)
+      load_v((u + C::NBUF - 1) % C::NBUF, vprev);
+      pv_mfma(vprev);
+    }
+    if (issue) gload_lds(t + AHEAD, (u + AHEAD) % C::NBUF);
     if constexpr (decltype(next_tag)::value) qk_mfma((u + 1) % C::NBUF, snext);
-    load_v(u, vcur);
-    constexpr bool sched = SCH == 1 && decltype(next_tag)::value && decltype(steady_tag)::value &&
-                           !decltype(masked_tag)::value;
+    if constexpr (!deferred) load_v(u, vcur);
+    constexpr bool sched = deferred && decltype(next_tag)::value && !decltype(masked_tag)::value;
     softmax(t, scur, masked_tag, std::integral_constant<bool, sched>{});
-    if constexpr (SCH == 0) pv_mfma(vcur);
-    if (issue && C::AHEAD > 2) __builtin_amdgcn_s_waitcnt(kWaitLgkm0VmCpt<C::CPT>);
+    if constexpr (!deferred) pv_mfma(vcur);
+    if (issue && AHEAD > 2) __builtin_amdgcn_s_waitcnt(kWaitLgkm0VmCpt<C::CPT>);
     else __builtin_amdgcn_s_waitcnt(kWaitAll);
     __asm__ volatile("s_barrier" ::: "memory");
   };
 
   // ---- prologue: tiles 0 .. AHEAD-1 in LDS, S^T(0) issued ----
 #pragma unroll
-  for (int i = 0; i < C::AHEAD; ++i)
+  for (int i = 0; i < AHEAD; ++i)
     if (i < ntiles) gload_lds(i, i);
+  if constexpr (SCH == 1) {
+    // V^T region of the last slot, read as "the previous tile" by tile 0
+    uint4* z = (uint4*)(smem + (C::NBUF - 1) * C::STAGE + C::KBYTES);
+    for (int i = tid; i < C::VCH; i += C::NT) z[i] = make_uint4(0, 0, 0, 0);
+  }
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
   v16i sA[2], sB[2];
   qk_mfma(0, sA);
-  // V^T operands of the even / odd tiles (SCH 1 multiplies the previous
-  // tile's at the start of each step: zero before tile 0 adds nothing)
+  // V^T operand registers of the even / odd tiles (every read fills them
+  // before its MFMAs)
   v8i vA[C::DC], vB[C::DC];
 #pragma unroll
   for (int dc = 0; dc < C::DC; ++dc) vA[dc] = vB[dc] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -411,11 +433,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
   // unrolled by the ring depth: the slot of every step is a constant
   const std::false_type no{};
   const std::true_type yes{};
-  for (; t + 3 + C::AHEAD < ntiles; t += 4) {  // every step of the group refills the ring
+  for (; t + 3 + AHEAD < ntiles; t += 4) {  // every step of the group refills the ring
     step(t, 0, sA, sB, vA, vB, no, yes, yes);
     step(t + 1, 1, sB, sA, vB, vA, no, yes, yes);
     step(t + 2, 2, sA, sB, vA, vB, no, yes, yes);
     step(t + 3, 3, sB, sA, vB, vA, no, yes, yes);
+  }
+  if constexpr (SCH == 1) {
+    if (t > 0) {  // the main loop ran: its last tile's PV is still pending
+      load_v((t + C::NBUF - 1) % C::NBUF, vB);
+      pv_mfma(vB);
+    }
   }
   for (; t + 4 < ntiles; t += 4) {
     step(t, 0, sA, sB, vA, vB, no, yes, no);
@@ -431,7 +459,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
                        v8i (&vprev)[C::DC]) __attribute__((always_inline)) {
     if (t < nfull) step(t, t % C::NBUF, scur, snext, vcur, vprev, no, no, no);
     else step(t, t % C::NBUF, scur, snext, vcur, vprev, yes, no, no);
-    if constexpr (SCH == 1) pv_mfma(vcur);  // the last tile's PV
   };
   // t is even here: S^T(t) is in sA, its V^T operands go to vA
   if (t + 1 < ntiles) {
@@ -513,9 +540,12 @@ hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
 #define SAGE_ATTN_LAUNCH(NWW, SCHH)                                                               \
   attn_launch<D, NWW, KB, SCHH>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H, \
                                 q_block, sm_scale, out, o_sb, o_sn, o_sh, stream)
-  const bool interleaved = attn_schedule() == 1;
-  if (attn_waves(B, Nq, H) == 8) return interleaved ? SAGE_ATTN_LAUNCH(8, 1) : SAGE_ATTN_LAUNCH(8, 0);
-  return interleaved ? SAGE_ATTN_LAUNCH(4, 1) : SAGE_ATTN_LAUNCH(4, 0);
+  // Default schedule: interleaved for four-wave workgroups (two per CU, whose
+  // waves do not share barriers), the compiler's order for eight-wave ones,
+  // where interleaving measured no faster.
+  const int sch = attn_schedule();
+  if (attn_waves(B, Nq, H) == 8) return sch == 1 ? SAGE_ATTN_LAUNCH(8, 1) : SAGE_ATTN_LAUNCH(8, 0);
+  return sch == 0 ? SAGE_ATTN_LAUNCH(4, 0) : SAGE_ATTN_LAUNCH(4, 1);
 #undef SAGE_ATTN_LAUNCH
 }
 

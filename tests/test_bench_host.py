@@ -71,6 +71,13 @@ def test_sp_shards_cover_the_sequence():
     assert bench.sp_shard(32760, 8, 7) == (28672, 32760)
 
 
+def test_attention_schedule_names():
+    # the default interleaves four-wave workgroups only; 1 and 2 force a schedule
+    assert [bench.attn_sch(w) for w in (4, 8)] == [1, 0]
+    assert [bench.attn_sch(w, 1) for w in (4, 8)] == [0, 0]
+    assert [bench.attn_sch(w, 2) for w in (4, 8)] == [1, 1]
+
+
 def test_abba_variant_parsing():
     assert bench.parse_variant("default") == {}
     assert bench.parse_variant("producer=fused;streams=1") == {"producer": "fused", "streams": 1}

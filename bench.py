@@ -550,9 +550,9 @@ def prewarm(run_step, torch, ms):
 
 def attn_sch(waves, schedule=0):
     """The attention kernel's schedule template argument for a launch of this
-    workgroup size under sage_attn_schedule(schedule): by default interleaved
-    (1) for four-wave workgroups, the compiler's order (0) for eight-wave ones."""
-    return {0: 1 if waves == 4 else 0, 1: 0, 2: 1}[schedule]
+    workgroup size under sage_attn_schedule(schedule): interleaved (1) by
+    default, the compiler's order (0) when forced with schedule 1."""
+    return {0: 1, 1: 0, 2: 1}[schedule]
 
 
 def parse_variant(spec):

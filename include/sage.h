@@ -396,10 +396,10 @@ int sage_attn_tuning(int waves_per_workgroup);
 
 /* Benchmark hook (process-wide, like sage_attn_tuning): forces the
  * instruction schedule of later sage_attn_fwd* launches: 0 the library's
- * default (2 for four-wave workgroups, 1 for eight-wave ones), 1 the
- * compiler's own order of each key step, 2 each step's MFMAs spread through
- * its softmax instructions (the previous tile's P.V first).  The output does
- * not depend on it (the same operations on the same values).
+ * default (2), 1 the compiler's own order of each key step, 2 each step's
+ * MFMAs spread through its softmax instructions (the previous tile's P.V
+ * first).  The output does not depend on it (the same operations on the same
+ * values).
  * Returns SAGE_OK or SAGE_ERR_VALUE. */
 int sage_attn_schedule(int schedule);
 

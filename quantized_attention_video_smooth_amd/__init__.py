@@ -179,9 +179,8 @@ def sage_attn_tuning(waves: int = 0) -> None:
 
 
 def sage_attn_schedule(schedule: int = 0) -> None:
-    """Benchmark hook: forced attention key-step schedule (0 default: 2 for
-    four-wave workgroups, 1 for eight-wave ones; 1 the compiler's order; 2
-    MFMAs spread through the softmax), process-wide."""
+    """Benchmark hook: forced attention key-step schedule (0 default, i.e. 2;
+    1 the compiler's order; 2 MFMAs spread through the softmax), process-wide."""
     _check(lib().sage_attn_schedule(schedule), "sage_attn_schedule")
 
 

@@ -28,9 +28,9 @@
 //     makes those bytes line up (sage_v_slot in sage.h);
 //   * software pipelining: S^T of tile t+1 is issued to the matrix cores before
 //     the softmax of tile t runs on the vector ALU, so the two overlap within
-//     a wave and across the two waves that share each SIMD; four-wave
-//     workgroups also defer the P.V of tile t to the next step and spread all
-//     12 MFMAs of a step through its softmax instructions;
+//     a wave and across the two waves that share each SIMD; the P.V of tile t
+//     is deferred to the next step and all 12 MFMAs of a step are spread
+//     through its softmax instructions;
 //   * exp2 with log2(e) and the static P scale 448 folded into one FMA; the
 //     accumulator rescale is skipped when no row max moved.
 #include <hip/hip_runtime.h>
@@ -50,9 +50,8 @@ void set_attn_waves(int waves) { g_attn_waves.store(waves, std::memory_order_rel
 // Key-step schedule forced for benchmark comparisons (0 = the default).
 static std::atomic<int> g_attn_sched{0};
 void set_attn_schedule(int schedule) { g_attn_sched.store(schedule, std::memory_order_relaxed); }
-// -1: the default (chosen by workgroup size), 0: the compiler's order,
-// 1: interleaved
-static int attn_schedule() { return g_attn_sched.load(std::memory_order_relaxed) - 1; }
+// 0: the compiler's order, 1: interleaved (the default)
+static int attn_schedule() { return g_attn_sched.load(std::memory_order_relaxed) == 1 ? 0 : 1; }
 
 namespace {
 
@@ -333,7 +332,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a PV MFMA (previous tile)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two K operand reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        // VALU instructions behind each PV MFMA (measured best: 8 with two
+        // workgroups per CU, 12 with one)
+        __builtin_amdgcn_sched_group_barrier(0x002, NW == 8 ? 12 : 8, 0);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -540,12 +541,9 @@ hipError_t attn_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
 #define SAGE_ATTN_LAUNCH(NWW, SCHH)                                                               \
   attn_launch<D, NWW, KB, SCHH>(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, v_mean, B, Nq, Nk, H, \
                                 q_block, sm_scale, out, o_sb, o_sn, o_sh, stream)
-  // Default schedule: interleaved for four-wave workgroups (two per CU, whose
-  // waves do not share barriers), the compiler's order for eight-wave ones,
-  // where interleaving measured no faster.
-  const int sch = attn_schedule();
-  if (attn_waves(B, Nq, H) == 8) return sch == 1 ? SAGE_ATTN_LAUNCH(8, 1) : SAGE_ATTN_LAUNCH(8, 0);
-  return sch == 0 ? SAGE_ATTN_LAUNCH(4, 0) : SAGE_ATTN_LAUNCH(4, 1);
+  const bool interleaved = attn_schedule() == 1;
+  if (attn_waves(B, Nq, H) == 8) return interleaved ? SAGE_ATTN_LAUNCH(8, 1) : SAGE_ATTN_LAUNCH(8, 0);
+  return interleaved ? SAGE_ATTN_LAUNCH(4, 1) : SAGE_ATTN_LAUNCH(4, 0);
 #undef SAGE_ATTN_LAUNCH
 }
 

@@ -72,8 +72,8 @@ def test_sp_shards_cover_the_sequence():
 
 
 def test_attention_schedule_names():
-    # the default interleaves four-wave workgroups only; 1 and 2 force a schedule
-    assert [bench.attn_sch(w) for w in (4, 8)] == [1, 0]
+    # the default is the interleaved schedule; 1 and 2 force a schedule
+    assert [bench.attn_sch(w) for w in (4, 8)] == [1, 1]
     assert [bench.attn_sch(w, 1) for w in (4, 8)] == [0, 0]
     assert [bench.attn_sch(w, 2) for w in (4, 8)] == [1, 1]
 

@@ -28,8 +28,12 @@ def sage():
     return s
 
 
-@pytest.mark.parametrize("shape", [(1, 300, 3, 64), (1, 1000, 2, 128), (2, 777, 5, 128), (1, 4608, 6, 128)],
-                         ids=["N300-D64", "N1000-D128", "B2-N777", "N4608"])
+# Key-tile counts: 5 (N300: no steady group, so no deferred PV), 6 (N384 and the
+# ragged N350: exactly one steady group, then the flush and the last steps),
+# 13, 16 and 72 (several groups).
+@pytest.mark.parametrize("shape", [(1, 300, 3, 64), (1, 384, 2, 128), (1, 350, 3, 64), (1, 1000, 2, 128),
+                                   (2, 777, 5, 128), (1, 4608, 6, 128)],
+                         ids=["N300-D64", "N384-D128", "N350-D64", "N1000-D128", "B2-N777", "N4608"])
 @pytest.mark.parametrize("k_block", [64, 16])
 @pytest.mark.parametrize("waves", [4, 8])
 def test_schedules_bit_identical(sage, shape, k_block, waves):

@@ -57,3 +57,31 @@ def test_schedules_bit_identical(sage, shape, k_block, waves):
     _log(f"  differing outputs: {int((a != b).sum())} of {a.numel()}")
     assert torch.isfinite(outs[0].float()).all()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("k_block", [64, 16])
+@pytest.mark.parametrize("waves", [4, 8])
+def test_forced_workgroup_size_against_oracle(sage, D, k_block, waves):
+    """The default schedule under either workgroup size (forced) against the
+    oracle's tiled attention, on a ragged key count with several steady groups
+    (13 key tiles): the default shapes reach eight-wave workgroups only at D=128
+    and with 64-token K blocks."""
+    import oracle
+    from tests.attn_bars import check_attention
+    B, N, H = 1, 777, 2
+    cfg = synth.custom(B, N, H, D, tag=510)
+    _log(f"[oracle] B{B} N{N} H{H} D{D} k_block {k_block} waves {waves}")
+    q, k, v = synth.make_qkv(cfg)
+    ref_qk, ref_v = oracle.quant_qk(q, k, k_block=k_block), oracle.quant_v(v)
+    qk = sage.quant_qk(q.cuda(), k.cuda(), k_block=k_block)
+    vq = sage.quant_v(v.cuda())
+    try:
+        sage.sage_attn_tuning(waves)
+        out = sage.attn_fwd(*qk[:4], *vq, N)
+        torch.cuda.synchronize()
+    finally:
+        sage.sage_attn_tuning(0)
+    got = out.float().cpu().permute(0, 2, 1, 3).double().numpy()
+    tiled = oracle.attn_tiled(ref_qk, ref_v)
+    check_attention(got, tiled, ref_v["v_mean"], log=_log)

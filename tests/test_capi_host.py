@@ -216,6 +216,29 @@ def test_attn_launch_shape(sage):
     assert sage.lib().sage_attn_launch_shape(1, 10, 2, 64, None, None) == -1
 
 
+def test_benchmark_hooks(sage):
+    """The process-wide benchmark hooks take exactly their documented values
+    (schedule 0..2; waves 0, 4 or 8) and a forced workgroup size shows in the
+    reported launch shape; both are reset afterwards."""
+    lib = sage.lib()
+    try:
+        for v in (0, 1, 2):
+            assert lib.sage_attn_schedule(v) == 0
+        for v in (-1, 3, 100):
+            assert lib.sage_attn_schedule(v) == -9  # SAGE_ERR_VALUE
+        for v in (0, 4, 8):
+            assert lib.sage_attn_tuning(v) == 0
+        for v in (-1, 1, 2, 16):
+            assert lib.sage_attn_tuning(v) == -9
+        assert lib.sage_attn_tuning(8) == 0
+        w, g = sage.sage_attn_launch_shape(2, 4608, 24, 128)
+        assert (w, g) == (8, 2 * 24 * 18)
+    finally:
+        lib.sage_attn_schedule(0)
+        lib.sage_attn_tuning(0)
+    assert sage.sage_attn_launch_shape(2, 4608, 24, 128)[0] == 4
+
+
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
     import quantized_attention_video_smooth_amd as s
     monkeypatch.setattr(s, "_lib", None)

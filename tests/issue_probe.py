@@ -30,4 +30,6 @@ def load():
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.probe_issue.argtypes = [i32, i32, i32, i32, vp, vp, vp]
     lib.probe_issue.restype = i32
+    lib.probe_pair.argtypes = [i32, i32, i32, i32, vp, vp, vp]
+    lib.probe_pair.restype = i32
     return lib

@@ -67,3 +67,32 @@ def test_issue_rates(probe):
     assert rates[(2, 2)] >= 1.5 * rates[(0, 2)]
     assert rates[(3, 2)] >= 1.5 * rates[(0, 2)]
     assert rates[(1, 2)] >= 0.8 * rates[(0, 2)]
+
+
+def test_matrix_and_vector_waves_overlap(probe):
+    """One SIMD's two waves, one running only FP8 MFMAs and one only a vector
+    instruction (each sized to take about as long alone as the other): how
+    much of the shorter one the pair hides.  In the attention each wave mixes
+    both units; its counters show 0.57-0.63 of the MFMA-busy cycles overlapped."""
+    mod, lib = probe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters_m = 1024
+    t_m = _cycles(lib, 5, 4, 1, iters_m, cus) * iters_m * 4       # one wave per SIMD, alone
+    seed = torch.linspace(-1.0, 1.0, 64, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(cus * 8, dtype=torch.int64, device="cuda")
+    sink = torch.empty(cus * 8 * 64, dtype=torch.float32, device="cuda")
+    hidden = {}
+    for vop in (0, 1, 2, 3):
+        name = mod.OPS[vop][0]
+        per = _cycles(lib, vop, 8, 1, 4096, cus)
+        iters_v = max(1, int(t_m / (8 * per)))
+        t_v = per * iters_v * 8
+        for _ in range(2):
+            st = lib.probe_pair(vop, cus, iters_m, iters_v, seed.data_ptr(), cyc.data_ptr(), sink.data_ptr())
+            assert st == 0, st
+        both = statistics.median(cyc.view(cus, 8).max(dim=1).values.cpu().tolist())
+        hidden[name] = (t_m + t_v - both) / min(t_m, t_v)
+        _log(f"MFMA-only wave alone {t_m:.0f} cycles, {name}-only wave alone {t_v:.0f}, the pair {both:.0f}: "
+             f"{100 * hidden[name]:.0f}% of the shorter one hidden")
+        # side by side, not one after the other
+        assert both <= 0.8 * (t_m + t_v)

@@ -339,7 +339,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an S^T MFMA (next tile)
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        if constexpr (NW == 8) {
+          // four exp2 right behind it, then other vector instructions
+          // (measured ~1% faster with one workgroup per CU, ~0.3% slower
+          // with two)
+          __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        }
       }
     }
     // Keep the exponentials and packs in this basic block, ahead of the
